@@ -1,0 +1,103 @@
+/*
+ * psa_attn.h — C ABI of libpsa_attn.so: PSA self-attention forward and
+ * backward over a conv feature map, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (PsaFa2Backward page, vision_rs psa kernels, struct
+ * description): Flash-Attention-2 style self-attention in which the query and
+ * key sequences are the same N = H*W tokens of one (batch, head) slice and
+ * every query attends to every key (no mask, no positional bias).  With
+ * Q, K in R^{N x dk}, V in R^{N x dv}, s = scale:
+ *
+ *   forward   S = s Q K^T,  LSE_i = ln sum_j exp(S_ij),  P = exp(S - LSE),
+ *             O = P V
+ *   backward  D_i = sum_c dO_ic O_ic,  dS = P o (dO V^T - D),
+ *             dQ = s dS K,  dK = s dS^T Q,  dV = P^T dO
+ *
+ * Layout (same page: packed buffer with sections 0/1/2 = Q/K/V, and the
+ * gradient buffer d_packed with sections 0/1/2 = dQ/dK/dV).  Every tensor is
+ * dense, contiguous and channel-major, tokens contiguous:
+ *   qkv, d_packed  [B, heads, 2*dk + dv, N]   channels [0,dk) Q, [dk,2dk) K,
+ *                                             [2dk, 2dk+dv) V
+ *   o, dO          [B, heads, dv, N]
+ *   lse            [B, heads, N]  float32 in every mode, natural log,
+ *                                 scale included
+ * Element type of qkv, o, dO and d_packed is given by `dtype`.
+ *
+ * Pointers are device pointers (hipMalloc'd or equivalent) that the caller
+ * owns; the library never frees or retains them.  Base addresses must be
+ * 16-byte aligned.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ * Calls are asynchronous: they validate, enqueue on `stream` and return.
+ * Results are valid once the stream has been synchronised.  On any
+ * validation failure nothing is enqueued, nothing is written, a status other
+ * than PSA_OK is returned and psa_last_error() describes it.  Faults during
+ * execution surface at the caller's next synchronisation.  Outputs are fully
+ * overwritten (no zero-initialisation is required).  NaN/Inf inputs
+ * propagate; they are not trapped.
+ */
+#ifndef PSA_ATTN_H
+#define PSA_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PSA_F32 = 0,  /* float32 storage, float32 arithmetic                    */
+  PSA_BF16 = 1  /* bfloat16 storage, bf16 MFMA with float32 accumulation  */
+} psa_dtype_t;
+
+typedef enum {
+  PSA_OK = 0,
+  PSA_ERR_NULL = 1,        /* a required pointer is NULL                  */
+  PSA_ERR_SHAPE = 2,       /* B, heads, N < 1, sizes overflow, bad scale  */
+  PSA_ERR_UNSUPPORTED = 3, /* (dk, dv, dtype) has no compiled instance    */
+  PSA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned       */
+  PSA_ERR_ALIAS = 5,       /* an output overlaps an input or other output */
+  PSA_ERR_NOMEM = 6,       /* library scratch could not be allocated      */
+  PSA_ERR_HIP = 7          /* a HIP runtime call or launch failed         */
+} psa_status_t;
+
+/*
+ * Forward: O and the row logsumexp LSE from the packed projection.
+ *   qkv  in   [B, heads, 2dk+dv, N], dtype
+ *   o    out  [B, heads, dv, N], dtype
+ *   lse  out  [B, heads, N], float32 (natural log of sum_j exp(s q_i.k_j))
+ *   scale     softmax scale s, finite and > 0 (usually 1/sqrt(dk))
+ * Scratch: none.
+ */
+int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N,
+                 int dk, int dv, float scale, int dtype, void* stream);
+
+/*
+ * Backward: the packed gradient of sum(dO o O) with respect to qkv.
+ *   qkv       in   [B, heads, 2dk+dv, N], dtype
+ *   o         in   [B, heads, dv, N], dtype  (D is formed from it as given)
+ *   lse       in   [B, heads, N], float32, as written by psa_attn_fwd
+ *   dO        in   [B, heads, dv, N], dtype
+ *   d_packed  out  [B, heads, 2dk+dv, N], dtype: section 0 = dQ,
+ *                  section 1 = dK, section 2 = dV, each element written
+ *                  exactly once (deterministic: bitwise identical results
+ *                  run to run; no floating-point atomics)
+ * Scratch: 8*B*heads*N bytes of device memory, taken stream-ordered from
+ * `stream` (hipMallocAsync) and released stream-ordered before returning.
+ */
+int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dO,
+                 void* d_packed, int B, int heads, int N, int dk, int dv, float scale,
+                 int dtype, void* stream);
+
+/* 1 if (dk, dv, dtype) has a compiled instance, else 0.  No GPU access. */
+int psa_attn_supported(int dk, int dv, int dtype);
+
+/* Message for the last non-OK status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the thread's next call. */
+const char* psa_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int psa_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_ATTN_H */

@@ -1,0 +1,143 @@
+"""Thin ctypes binding of libpsa_attn.so.
+
+The names mirror the C ABI in include/psa_attn.h one to one and only marshal
+arguments; every step of the computation runs in the HIP kernels.  PyTorch is
+used for device memory and the current stream, nothing else.  There is no
+fallback: if the library is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+PSA_F32 = 0
+PSA_BF16 = 1
+
+STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
+          4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
+
+EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_supported", "psa_last_error",
+           "psa_attn_version")
+
+_lib = None
+
+
+class PsaError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (once) and return the library; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with vision_transformer_attention_psa_amd.build "
+                           "(or __graft_entry__.build()) before use")
+    lib = ctypes.CDLL(p)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.psa_attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.psa_attn_fwd.restype = i
+    lib.psa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.psa_attn_bwd.restype = i
+    lib.psa_attn_supported.argtypes = [i, i, i]
+    lib.psa_attn_supported.restype = i
+    lib.psa_last_error.argtypes = []
+    lib.psa_last_error.restype = ctypes.c_char_p
+    lib.psa_attn_version.argtypes = []
+    lib.psa_attn_version.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def psa_last_error() -> str:
+    return load().psa_last_error().decode()
+
+
+def psa_attn_supported(dk: int, dv: int, dtype: int) -> bool:
+    return bool(load().psa_attn_supported(dk, dv, dtype))
+
+
+def psa_attn_version() -> int:
+    return load().psa_attn_version()
+
+
+def psa_attn_fwd(qkv: int, o: int, lse: int, B: int, heads: int, N: int, dk: int, dv: int,
+                 scale: float, dtype: int, stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_attn_fwd(qkv, o, lse, B, heads, N, dk, dv, scale, dtype, stream)
+
+
+def psa_attn_bwd(qkv: int, o: int, lse: int, dO: int, d_packed: int, B: int, heads: int, N: int,
+                 dk: int, dv: int, scale: float, dtype: int, stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_attn_bwd(qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, scale, dtype, stream)
+
+
+# ------------------------------------------------------------ torch helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PSA_F32
+    if t.dtype == torch.bfloat16:
+        return PSA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise PsaError(fn, rc, psa_last_error())
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _shape(qkv, dk: int, dv: int):
+    if qkv.dim() != 4 or qkv.shape[2] != 2 * dk + dv:
+        raise ValueError(f"qkv must be [B, heads, 2*dk+dv, N]; got {tuple(qkv.shape)}")
+    if not qkv.is_contiguous():
+        raise ValueError("qkv must be contiguous")
+    B, H, _, N = qkv.shape
+    return B, H, N
+
+
+def fwd(qkv, dk: int, dv: int, scale: float, out=None):
+    """O [B, heads, dv, N] (qkv's dtype) and LSE [B, heads, N] (float32)."""
+    import torch
+    B, H, N = _shape(qkv, dk, dv)
+    if out is None:
+        o = torch.empty((B, H, dv, N), dtype=qkv.dtype, device=qkv.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
+    else:
+        o, lse = out
+    _check("psa_attn_fwd", psa_attn_fwd(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, dk,
+                                        dv, float(scale), _dtype_code(qkv), _stream(qkv)))
+    return o, lse
+
+
+def bwd(qkv, o, lse, dO, dk: int, dv: int, scale: float, out=None):
+    """d_packed [B, heads, 2dk+dv, N]: sections dQ, dK, dV."""
+    import torch
+    B, H, N = _shape(qkv, dk, dv)
+    for name, t in (("o", o), ("lse", lse), ("dO", dO)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tuple(o.shape) != (B, H, dv, N) or tuple(dO.shape) != (B, H, dv, N):
+        raise ValueError("o and dO must be [B, heads, dv, N]")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, heads, N]")
+    if o.dtype != qkv.dtype or dO.dtype != qkv.dtype:
+        raise ValueError("o and dO must have qkv's dtype")
+    d = torch.empty_like(qkv) if out is None else out
+    _check("psa_attn_bwd", psa_attn_bwd(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), dO.data_ptr(),
+                                        d.data_ptr(), B, H, N, dk, dv, float(scale),
+                                        _dtype_code(qkv), _stream(qkv)))
+    return d

@@ -1,0 +1,237 @@
+// libpsa_attn.so: C ABI for PSA self-attention forward and backward on
+// MI355X (gfx950).  Argument meaning, layouts, ownership and error behaviour
+// are specified in include/psa_attn.h; this file validates, picks the
+// compiled instance for (dtype, dk, dv) and enqueues on the caller's stream.
+#include "psa_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "psa_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+// Tile shapes per element type.  bf16 fragments take half the registers of
+// fp32 ones, so bf16 tiles are twice as wide in the stationary dimension.
+template <typename T> struct Tiles;
+template <> struct Tiles<psa::bf16> {
+  static constexpr int FWD_NW = 4, FWD_QB = 2, FWD_BN = 64;
+  static constexpr int DKDV_NW = 4, DKDV_KB = 2, DKDV_BMQ = 64;
+  static constexpr int DQ_NW = 4, DQ_QB = 2, DQ_BN = 64;
+};
+template <> struct Tiles<float> {
+  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
+  static constexpr int DKDV_NW = 4, DKDV_KB = 1, DKDV_BMQ = 32;
+  static constexpr int DQ_NW = 4, DQ_QB = 1, DQ_BN = 32;
+};
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return PSA_OK;
+}
+
+template <typename T> constexpr bool vec_ok(int N) { return N % (16 / (int)sizeof(T)) == 0; }
+
+template <typename T, int DK, int DV>
+int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hipStream_t st) {
+  using C = Tiles<T>;
+  constexpr int BM = C::FWD_NW * 16 * C::FWD_QB;
+  const int nqt = (N + BM - 1) / BM;
+  const long long grid = (long long)BH * nqt;
+  if (grid > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_attn_fwd: grid too large");
+  const float c = scale * psa::kLog2e;
+  const dim3 g((unsigned)grid), b(C::FWD_NW * 64);
+  if (vec_ok<T>(N))
+    hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true>), g, b, 0, st,
+                       (const T*)qkv, (T*)o, lse, N, nqt, c);
+  else
+    hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, false>), g, b, 0, st,
+                       (const T*)qkv, (T*)o, lse, N, nqt, c);
+  return check_launch("psa_attn_fwd launch");
+}
+
+template <typename T, int DK, int DV>
+int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, void* dpk, int BH, int N,
+            float scale, hipStream_t st) {
+  using C = Tiles<T>;
+  const float c = scale * psa::kLog2e;
+  const long long total = (long long)BH * N;
+  constexpr int BNK = C::DKDV_NW * 16 * C::DKDV_KB;
+  constexpr int BMD = C::DQ_NW * 16 * C::DQ_QB;
+  const int nkt = (N + BNK - 1) / BNK, nqt = (N + BMD - 1) / BMD;
+  if ((long long)BH * nkt > INT32_MAX || (long long)BH * nqt > INT32_MAX)
+    return fail(PSA_ERR_SHAPE, "psa_attn_bwd: grid too large");
+
+  float2* stats = nullptr;
+  hipError_t e = hipMallocAsync((void**)&stats, (size_t)total * sizeof(float2), st);
+  if (e != hipSuccess || stats == nullptr)
+    return fail(PSA_ERR_NOMEM, std::string("psa_attn_bwd: scratch allocation failed: ") + hipGetErrorString(e));
+
+  hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+  int rc = check_launch("psa_attn_bwd preprocess launch");
+  if (rc == PSA_OK) {
+    const dim3 gk((unsigned)(BH * nkt)), bk(C::DKDV_NW * 64);
+    if (vec_ok<T>(N))
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_NW, C::DKDV_BMQ, true>), gk, bk, 0,
+                         st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
+    else
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_NW, C::DKDV_BMQ, false>), gk, bk,
+                         0, st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
+    rc = check_launch("psa_attn_bwd dK/dV launch");
+  }
+  if (rc == PSA_OK) {
+    const dim3 gq((unsigned)(BH * nqt)), bq(C::DQ_NW * 64);
+    if (vec_ok<T>(N))
+      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, C::DQ_NW, C::DQ_BN, true>), gq, bq, 0, st,
+                         (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
+    else
+      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, C::DQ_NW, C::DQ_BN, false>), gq, bq, 0, st,
+                         (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
+    rc = check_launch("psa_attn_bwd dQ launch");
+  }
+  e = hipFreeAsync(stats, st);
+  if (rc == PSA_OK && e != hipSuccess)
+    rc = fail(PSA_ERR_HIP, std::string("psa_attn_bwd: scratch release failed: ") + hipGetErrorString(e));
+  return rc;
+}
+
+// ------------------------------------------------------------ instance table
+#define PSA_INSTANCES(X)   \
+  X(PSA_F32, float, 16, 16)     \
+  X(PSA_F32, float, 32, 32)     \
+  X(PSA_F32, float, 32, 64)     \
+  X(PSA_F32, float, 64, 64)     \
+  X(PSA_BF16, psa::bf16, 32, 32) \
+  X(PSA_BF16, psa::bf16, 32, 64) \
+  X(PSA_BF16, psa::bf16, 64, 64)
+
+bool supported(int dk, int dv, int dtype) {
+#define X(DT, T, K, V) if (dtype == DT && dk == K && dv == V) return true;
+  PSA_INSTANCES(X)
+#undef X
+  return false;
+}
+
+size_t elem_size(int dtype) { return dtype == PSA_F32 ? 4 : 2; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shape/pointer validation shared by both entry points.
+int validate_common(const char* fn, int B, int heads, int N, int dk, int dv, float scale, int dtype) {
+  if (dtype != PSA_F32 && dtype != PSA_BF16) return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": unknown dtype");
+  if (B < 1 || heads < 1 || N < 1 || dk < 1 || dv < 1)
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": B, heads, N, dk, dv must all be >= 1");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": scale must be finite and > 0");
+  const __int128 BH = (__int128)B * heads;
+  const __int128 elems = BH * (2 * (__int128)dk + dv) * N;
+  if (BH * N > INT32_MAX || elems > ((__int128)1 << 46))
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": problem too large");
+  if (!supported(dk, dv, dtype)) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "%s: no compiled instance for dk=%d dv=%d dtype=%s", fn, dk, dv,
+             dtype == PSA_F32 ? "f32" : "bf16");
+    return fail(PSA_ERR_UNSUPPORTED, buf);
+  }
+  return PSA_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+// gfx950 is the only compiled target; refuse other devices before any launch.
+int check_device(const char* fn) {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 ok, 2 wrong arch
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PSA_ERR_HIP, std::string(fn) + ": no HIP device");
+  if (dev < 0 || dev >= 64) return fail(PSA_ERR_HIP, std::string(fn) + ": device index out of range");
+  std::lock_guard<std::mutex> lk(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(PSA_ERR_HIP, std::string(fn) + ": hipGetDeviceProperties failed");
+    known[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 2;
+  }
+  if (known[dev] != 1) return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": device is not gfx950");
+  return PSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int psa_attn_supported(int dk, int dv, int dtype) { return supported(dk, dv, dtype) ? 1 : 0; }
+
+const char* psa_last_error(void) { return g_err.c_str(); }
+
+int psa_attn_version(void) { return 100; }
+
+int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N, int dk, int dv, float scale,
+                 int dtype, void* stream) {
+  g_err.clear();
+  const char* fn = "psa_attn_fwd";
+  if (!qkv || !o || !lse) return fail(PSA_ERR_NULL, "psa_attn_fwd: qkv, o and lse must be non-NULL");
+  int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
+  if (rc != PSA_OK) return rc;
+  if (misaligned(qkv) || misaligned(o) || misaligned(lse))
+    return fail(PSA_ERR_ALIGN, "psa_attn_fwd: base pointers must be 16-byte aligned");
+  const size_t e = elem_size(dtype), BH = (size_t)B * heads;
+  const Range rq{(uintptr_t)qkv, (uintptr_t)qkv + BH * (2 * dk + dv) * N * e};
+  const Range ro{(uintptr_t)o, (uintptr_t)o + BH * dv * N * e};
+  const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
+  if (overlap(ro, rq) || overlap(rl, rq) || overlap(ro, rl))
+    return fail(PSA_ERR_ALIAS, "psa_attn_fwd: o, lse and qkv must not overlap");
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+#define X(DT, T, K, V) \
+  if (dtype == DT && dk == K && dv == V) return run_fwd<T, K, V>(qkv, o, lse, (int)BH, N, scale, st);
+  PSA_INSTANCES(X)
+#undef X
+  return fail(PSA_ERR_UNSUPPORTED, "psa_attn_fwd: no instance");
+}
+
+int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed, int B,
+                 int heads, int N, int dk, int dv, float scale, int dtype, void* stream) {
+  g_err.clear();
+  const char* fn = "psa_attn_bwd";
+  if (!qkv || !o || !lse || !dO || !d_packed)
+    return fail(PSA_ERR_NULL, "psa_attn_bwd: qkv, o, lse, dO and d_packed must be non-NULL");
+  int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
+  if (rc != PSA_OK) return rc;
+  if (misaligned(qkv) || misaligned(o) || misaligned(lse) || misaligned(dO) || misaligned(d_packed))
+    return fail(PSA_ERR_ALIGN, "psa_attn_bwd: base pointers must be 16-byte aligned");
+  const size_t e = elem_size(dtype), BH = (size_t)B * heads;
+  const Range rd{(uintptr_t)d_packed, (uintptr_t)d_packed + BH * (2 * dk + dv) * N * e};
+  const Range rq{(uintptr_t)qkv, (uintptr_t)qkv + BH * (2 * dk + dv) * N * e};
+  const Range ro{(uintptr_t)o, (uintptr_t)o + BH * dv * N * e};
+  const Range rg{(uintptr_t)dO, (uintptr_t)dO + BH * dv * N * e};
+  const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
+  if (overlap(rd, rq) || overlap(rd, ro) || overlap(rd, rg) || overlap(rd, rl))
+    return fail(PSA_ERR_ALIAS, "psa_attn_bwd: d_packed must not overlap any input");
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+#define X(DT, T, K, V) \
+  if (dtype == DT && dk == K && dv == V) return run_bwd<T, K, V>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st);
+  PSA_INSTANCES(X)
+#undef X
+  return fail(PSA_ERR_UNSUPPORTED, "psa_attn_bwd: no instance");
+}
+
+}  // extern "C"
