@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the PSA attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: psa_attn_fwd (O, LSE)
+then psa_attn_bwd (D/LSE preprocess, dK/dV, dQ) on resident synthetic
+inputs.  Prints ONE JSON line.
+
+  value         backward TFLOP/s on the headline workload, algorithmic flops
+                BH * 2N^2 (3dk + 2dv) over the backward's event-timed duration
+  ms_per_step   wall time per fwd+bwd step (synchronised on both sides)
+  roofline      the dominant kernel: algorithmic flops per launch / average
+                launch duration from hipEvents recorded by the library around
+                each launch on its stream, against the bf16 dense MFMA peak
+  cpu_baseline  the float64 oracle timed on the host cores on a bounded
+                sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "PSA attn bwd TFLOP/s + µs/call (B=16,N=400 & N=6400), % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "highres_n6400_bf16"
+ALSO = ("batched_n400_bf16", "midres_n1600_bf16")
+
+
+def flops(wl) -> dict:
+    """Algorithmic flops per call for the whole batch (per (b,h) slice x BH)."""
+    n2 = 2.0 * wl.N * wl.N * wl.BH
+    return {
+        "fwd": n2 * (wl.dk + wl.dv),                 # S = QK^T, O = PV
+        "bwd": n2 * (3 * wl.dk + 2 * wl.dv),         # S recompute, dP, dV, dK, dQ
+        "fwd_dkdv": n2 * (2 * wl.dk + 2 * wl.dv),    # kernel: S, dP, dV, dK
+        "bwd_dq": n2 * (2 * wl.dk + wl.dv),          # kernel: S, dP, dQ (S, dP recomputed)
+    }
+
+
+def hbm_bytes(wl, e: int) -> dict:
+    """Algorithmic HBM bytes per call (compulsory reads/writes, whole batch)."""
+    N, BH, dk, dv = wl.N, wl.BH, wl.dk, wl.dv
+    return {
+        "fwd": BH * (e * N * (2 * dk + 2 * dv) + 4 * N),
+        "bwd": BH * (e * N * (2 * (2 * dk + dv) + 2 * dv) + 4 * N),
+        "bwd_pre": BH * (2 * e * N * dv + 4 * N + 8 * N),
+    }
+
+
+def device_inputs(torch, x):
+    import numpy as np
+    from vision_transformer_attention_psa_amd import inputs
+    if x.wl.dtype == inputs.BF16:
+        q = torch.from_numpy(x.qkv_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        g = torch.from_numpy(x.dO_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        q, g = torch.from_numpy(x.qkv).cuda(), torch.from_numpy(x.dO).cuda()
+    return q, g
+
+
+def time_workload(torch, wl, steps: int, warmup: int) -> dict:
+    from vision_transformer_attention_psa_amd import binding, inputs
+    x = inputs.make_inputs(wl)
+    qkv, dO = device_inputs(torch, x)
+    o = torch.empty((wl.B, wl.heads, wl.dv, wl.N), dtype=qkv.dtype, device="cuda")
+    lse = torch.empty((wl.B, wl.heads, wl.N), dtype=torch.float32, device="cuda")
+    d = torch.empty_like(qkv)
+
+    def step():
+        binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+        binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.psa_attn_timing_reset()
+    binding.psa_attn_timing_enable(True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record()
+        binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+        ev[k][1].record()
+        binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    binding.psa_attn_timing_enable(False)
+    kern = binding.psa_attn_timing_read()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    assert torch.isfinite(d.float()).all().item(), "non-finite gradient"
+    fl = flops(wl)
+    dt = "bf16" if wl.dtype == inputs.BF16 else "f32"
+    peak = PEAK_TFLOPS[dt]
+    avg = {k: (ms / n if n else float("nan")) for k, (ms, n) in kern.items()}
+    return {
+        "ms_per_step": (t1 - t0) * 1e3 / steps,
+        "fwd_us": fwd_ms * 1e3,
+        "bwd_us": bwd_ms * 1e3,
+        "fwd_tflops": fl["fwd"] / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": fl["bwd"] / (bwd_ms * 1e-3) / 1e12,
+        "fwd_bwd_tflops": (fl["fwd"] + fl["bwd"]) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
+        "bwd_pct_mfma_peak": 100.0 * fl["bwd"] / (bwd_ms * 1e-3) / 1e12 / peak,
+        "fwd_bwd_pct_mfma_peak": 100.0 * (fl["fwd"] + fl["bwd"]) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12 / peak,
+        "kernel_avg_us": {k: v * 1e3 for k, v in avg.items()},
+        "peak_tflops": peak,
+        "dtype": dt,
+    }
+
+
+def roofline(wl, r: dict, traffic: dict | None) -> dict:
+    """Dominant kernel of the step (largest average duration)."""
+    fl = flops(wl)
+    per_launch = {"fwd": fl["fwd"], "bwd_dkdv": fl["fwd_dkdv"], "bwd_dq": fl["bwd_dq"]}
+    us = r["kernel_avg_us"]
+    name = max(per_launch, key=lambda k: us[k])
+    achieved = per_launch[name] / (us[name] * 1e-6) / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": r["peak_tflops"],
+            "unit": "TFLOP/s", "frac": achieved / r["peak_tflops"], "avg_us": us[name],
+            "flops_per_launch": per_launch[name],
+            "traffic": (traffic or {}).get(name)}
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The float64 oracle on whole (b,h) slices of the same workload until
+    about `budget_s` seconds of CPU work have run (at least one slice)."""
+    from oracle import psa_oracle as orc
+    from vision_transformer_attention_psa_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    one = wl.with_(B=1, heads=1)
+    fl = flops(one)
+    fwd_s = bwd_s = 0.0
+    n = 0
+    while n < wl.BH and (n == 0 or fwd_s + bwd_s < budget_s):
+        x = inputs.make_inputs(one, seed=wl.seed * 1000 + n)
+        t0 = time.perf_counter()
+        o, lse = orc.forward(x.qkv, one.dk, one.dv, one.scale)
+        t1 = time.perf_counter()
+        orc.backward(x.qkv, o, lse, x.dO, one.dk, one.dv, one.scale)
+        t2 = time.perf_counter()
+        fwd_s += t1 - t0
+        bwd_s += t2 - t1
+        n += 1
+    return {"value": fl["bwd"] * n / bwd_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {wl.BH} (b,h) slices of {wl.name} (N={wl.N}, dk={wl.dk}, "
+                      f"dv={wl.dv}), float64 numpy; bwd {bwd_s / n * 1e3:.0f} ms/slice, "
+                      f"fwd {fwd_s / n * 1e3:.0f} ms/slice; BLAS threads={threads}",
+            "bwd_us_per_call_extrapolated": bwd_s / n * wl.BH * 1e6,
+            "fwd_us_per_call_extrapolated": fwd_s / n * wl.BH * 1e6}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--also", default=",".join(ALSO), help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--traffic-json", default=None,
+                    help="per-kernel HBM bytes per launch measured with rocprofv3 counters")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on exactly one GPU (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); every (batch, head) slice is independent and the multi-GPU "
+              "split is a host-side partition of B*heads, which is not benchmarked here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from vision_transformer_attention_psa_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    wl = inputs.WORKLOADS[args.workload]
+    print(f"[bench] {wl.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    r = time_workload(torch, wl, args.steps, args.warmup)
+    print(f"[bench] {wl.name}: fwd {r['fwd_us']:.1f} us, bwd {r['bwd_us']:.1f} us, "
+          f"bwd {r['bwd_tflops']:.1f} TFLOP/s, kernels {r['kernel_avg_us']}", file=sys.stderr, flush=True)
+    also = {}
+    for name in [a for a in args.also.split(",") if a]:
+        a = time_workload(torch, inputs.WORKLOADS[name], args.steps, args.warmup)
+        also[name] = {k: a[k] for k in ("fwd_us", "bwd_us", "bwd_tflops", "bwd_pct_mfma_peak",
+                                        "fwd_bwd_tflops", "fwd_bwd_pct_mfma_peak", "kernel_avg_us")}
+        print(f"[bench] {name}: fwd {a['fwd_us']:.1f} us, bwd {a['bwd_us']:.1f} us, "
+              f"bwd {a['bwd_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    traffic = None
+    if args.traffic_json and os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            traffic = json.load(f).get(wl.name)
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] cpu baseline: oracle on {wl.name} slices (~{args.cpu_budget:.0f} s)",
+              file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_budget)
+    out = {
+        "metric": METRIC,
+        "value": r["bwd_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r["dtype"],
+        "data": "synthetic (seeded i.i.d. normal, bf16-rounded)",
+        "config": {"workload": wl.name, "B": wl.B, "heads": wl.heads, "N": wl.N, "dk": wl.dk,
+                   "dv": wl.dv, "step": "psa_attn_fwd + psa_attn_bwd"},
+        "bwd_us_per_call": r["bwd_us"],
+        "bwd_pct_mfma_peak": r["bwd_pct_mfma_peak"],
+        "fwd_us_per_call": r["fwd_us"],
+        "fwd_bwd_tflops": r["fwd_bwd_tflops"],
+        "fwd_bwd_pct_mfma_peak": r["fwd_bwd_pct_mfma_peak"],
+        "kernel_avg_us": r["kernel_avg_us"],
+        "roofline": roofline(wl, r, traffic),
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

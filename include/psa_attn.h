@@ -96,6 +96,24 @@ const char* psa_last_error(void);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int psa_attn_version(void);
 
+/*
+ * Per-kernel device timing, for profiling and roofline reporting.  When
+ * enabled, every kernel launch inside psa_attn_fwd / psa_attn_bwd is
+ * bracketed by two hipEvents recorded on the launch stream; durations are
+ * accumulated per kernel.  Off by default; process-wide, thread-safe.
+ * Kernel slots: 0 = forward, 1 = backward preprocess (D, LSE*log2 e),
+ * 2 = backward dK/dV, 3 = backward dQ.
+ */
+#define PSA_TIMING_SLOTS 4
+/* on != 0 enables, 0 disables.  Returns PSA_OK. */
+int psa_attn_timing_enable(int on);
+/* Waits for every recorded launch, then writes min(n, PSA_TIMING_SLOTS)
+ * accumulated milliseconds and launch counts (either pointer may be NULL).
+ * Returns PSA_OK or PSA_ERR_HIP. */
+int psa_attn_timing_read(double* ms, long long* launches, int n);
+/* Drops all accumulated and pending measurements.  Returns PSA_OK. */
+int psa_attn_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

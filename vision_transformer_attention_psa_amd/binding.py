@@ -19,7 +19,9 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPP
           4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
 
 EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_supported", "psa_last_error",
-           "psa_attn_version")
+           "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
+           "psa_attn_timing_reset")
+TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
 
 _lib = None
 
@@ -51,6 +53,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.psa_last_error.restype = ctypes.c_char_p
     lib.psa_attn_version.argtypes = []
     lib.psa_attn_version.restype = i
+    lib.psa_attn_timing_enable.argtypes = [i]
+    lib.psa_attn_timing_enable.restype = i
+    lib.psa_attn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_longlong), i]
+    lib.psa_attn_timing_read.restype = i
+    lib.psa_attn_timing_reset.argtypes = []
+    lib.psa_attn_timing_reset.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -66,6 +75,23 @@ def psa_attn_supported(dk: int, dv: int, dtype: int) -> bool:
 
 def psa_attn_version() -> int:
     return load().psa_attn_version()
+
+
+def psa_attn_timing_enable(on: bool) -> int:
+    return load().psa_attn_timing_enable(1 if on else 0)
+
+
+def psa_attn_timing_reset() -> int:
+    return load().psa_attn_timing_reset()
+
+
+def psa_attn_timing_read() -> dict:
+    """{slot: (total_ms, launches)} for the four kernel slots."""
+    n = len(TIMING_SLOTS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_longlong * n)()
+    _check("psa_attn_timing_read", load().psa_attn_timing_read(ms, cnt, n))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(TIMING_SLOTS)}
 
 
 def psa_attn_fwd(qkv: int, o: int, lse: int, B: int, heads: int, N: int, dk: int, dv: int,

@@ -19,7 +19,13 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 OFFLOAD_ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in ordinary VGPRs: the softmax reads and
+                # rescales them with VALU ops, which cannot address AGPRs
+                "-mllvm", "-amdgpu-mfma-vgpr-form",
+                # non-IEEE mode: max/min need no NaN canonicalisation (device code
+                # only; the host-side argument checks still see real NaNs)
+                "-Xarch_device", "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans"]
 
 
 def hipcc() -> str:

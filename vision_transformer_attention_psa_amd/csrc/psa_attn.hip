@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "psa_kernels.h"
 
@@ -27,14 +28,67 @@ int fail(int code, const std::string& msg) {
 // fp32 ones, so bf16 tiles are twice as wide in the stationary dimension.
 template <typename T> struct Tiles;
 template <> struct Tiles<psa::bf16> {
-  static constexpr int FWD_NW = 4, FWD_QB = 2, FWD_BN = 64;
+  static constexpr int FWD_NW = 4, FWD_QB = 4, FWD_BN = 64;
   static constexpr int DKDV_NW = 4, DKDV_KB = 2, DKDV_BMQ = 64;
-  static constexpr int DQ_NW = 4, DQ_QB = 2, DQ_BN = 64;
+  static constexpr int DQ_NW = 4, DQ_QB = 4, DQ_BN = 64;
 };
 template <> struct Tiles<float> {
-  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
+  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
   static constexpr int DKDV_NW = 4, DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_NW = 4, DQ_QB = 1, DQ_BN = 32;
+};
+
+// ------------------------------------------------------- per-kernel timing
+enum { K_FWD = 0, K_PRE = 1, K_DKDV = 2, K_DQ = 3 };
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    int slot;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[PSA_TIMING_SLOTS] = {0};
+  long long n[PSA_TIMING_SLOTS] = {0};
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Timing g_timing;
+
+// Brackets one launch with events when timing is enabled.
+struct TimedLaunch {
+  int slot;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  TimedLaunch(int s, hipStream_t stream) : slot(s), st(stream) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.on && (a = g_timing.get()) != nullptr && hipEventRecord(a, st) != hipSuccess) {
+      g_timing.pool.push_back(a);
+      a = nullptr;
+    }
+  }
+  ~TimedLaunch() {
+    if (!a) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    hipEvent_t b = g_timing.get();
+    if (b && hipEventRecord(b, st) == hipSuccess) {
+      g_timing.pending.push_back({slot, a, b});
+    } else {
+      g_timing.pool.push_back(a);
+      if (b) g_timing.pool.push_back(b);
+    }
+  }
 };
 
 int check_launch(const char* what) {
@@ -54,6 +108,7 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hi
   if (grid > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_attn_fwd: grid too large");
   const float c = scale * psa::kLog2e;
   const dim3 g((unsigned)grid), b(C::FWD_NW * 64);
+  TimedLaunch tl(K_FWD, st);
   if (vec_ok<T>(N))
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true>), g, b, 0, st,
                        (const T*)qkv, (T*)o, lse, N, nqt, c);
@@ -80,11 +135,16 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   if (e != hipSuccess || stats == nullptr)
     return fail(PSA_ERR_NOMEM, std::string("psa_attn_bwd: scratch allocation failed: ") + hipGetErrorString(e));
 
-  hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     (const T*)o, (const T*)dO, lse, stats, N, (int)total);
-  int rc = check_launch("psa_attn_bwd preprocess launch");
+  int rc;
+  {
+    TimedLaunch tl(K_PRE, st);
+    hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                       (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+    rc = check_launch("psa_attn_bwd preprocess launch");
+  }
   if (rc == PSA_OK) {
     const dim3 gk((unsigned)(BH * nkt)), bk(C::DKDV_NW * 64);
+    TimedLaunch tl(K_DKDV, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_NW, C::DKDV_BMQ, true>), gk, bk, 0,
                          st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
@@ -95,6 +155,7 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   }
   if (rc == PSA_OK) {
     const dim3 gq((unsigned)(BH * nqt)), bq(C::DQ_NW * 64);
+    TimedLaunch tl(K_DQ, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, C::DQ_NW, C::DQ_BN, true>), gq, bq, 0, st,
                          (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
@@ -182,6 +243,49 @@ int psa_attn_supported(int dk, int dv, int dtype) { return supported(dk, dv, dty
 const char* psa_last_error(void) { return g_err.c_str(); }
 
 int psa_attn_version(void) { return 100; }
+
+int psa_attn_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return PSA_OK;
+}
+
+int psa_attn_timing_read(double* ms, long long* launches, int n) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  int rc = PSA_OK;
+  for (auto& r : g_timing.pending) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      rc = fail(PSA_ERR_HIP, "psa_attn_timing_read: event query failed");
+    } else {
+      g_timing.ms[r.slot] += t;
+      g_timing.n[r.slot] += 1;
+    }
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.pending.clear();
+  for (int k = 0; k < n && k < PSA_TIMING_SLOTS; ++k) {
+    if (ms) ms[k] = g_timing.ms[k];
+    if (launches) launches[k] = g_timing.n[k];
+  }
+  return rc;
+}
+
+int psa_attn_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& r : g_timing.pending) {
+    (void)hipEventSynchronize(r.b);
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.pending.clear();
+  for (int k = 0; k < PSA_TIMING_SLOTS; ++k) {
+    g_timing.ms[k] = 0;
+    g_timing.n[k] = 0;
+  }
+  return PSA_OK;
+}
 
 int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N, int dk, int dv, float scale,
                  int dtype, void* stream) {

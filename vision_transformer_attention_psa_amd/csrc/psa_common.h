@@ -1,20 +1,25 @@
 // Shared device building blocks for the PSA attention kernels on gfx950.
 //
-// Data in HBM is channel-major: every operand row is one channel and the
-// tokens are contiguous.  Tiles are staged into LDS in that same natural
-// layout ([channel][token], padded rows) and MFMA operands are read from it
-// in two ways:
-//   load_nat : MFMA row = channel, contraction over tokens (two 8/16-byte
-//              reads per lane, straight from the natural layout)
-//   load_tr  : MFMA row = token, contraction over channels.  bf16 uses the
-//              gfx950 LDS transpose read (ds_read_b64_tr_b16); fp32 reads
-//              one element per contraction slot.
-// Both produce the same fragment shape: a 16-row x 32-contraction chunk in
-// which lane l = row + 16*g holds 8 values and slot s carries contraction
-// index kmap(g, s) = 16*(s/4) + 4*g + (s%4).  That ordering is exactly how a
-// 16x16 fp32 accumulator block holds its rows (lane col + 16*g, register r ->
-// row 4*g + r), so two stacked accumulator blocks convert to a B operand
-// without any data movement across lanes (acc_to_frag).
+// Data in HBM is channel-major: each operand row is one channel and the
+// tokens are contiguous.  MFMA operands are 16-row x 32-contraction chunks
+// ("fragments"): lane l = row + 16*g holds 8 values, slot s carrying
+// contraction index 8*g + s.  The two kinds of fragment the attention GEMMs
+// need are
+//   frag_ch  : rows = channels, contraction over 32 tokens.  Read straight
+//              from a channel-major LDS tile ([channel][token]).
+//   frag_tok : rows = tokens, contraction over 32 channels.  bf16 reads it
+//              from a token-major LDS copy ([token][channel]) that the
+//              staging code writes once per tile (in-register 4x8 block
+//              transpose); fp32 gathers it from the channel-major tile.
+// Both are one 16-byte LDS read per lane for bf16.
+//
+// Chaining: a 16x16 fp32 accumulator block holds row 4*g + r of column
+// (lane & 15) in register r.  Score tiles are computed over 32-token chunks
+// whose rows are permuted: block h, row m <-> token 8*(m/4) + 4*h + m%4.
+// Then lane (col, g) holds tokens 8g..8g+3 in block 0 and 8g+4..8g+7 in
+// block 1, i.e. exactly the slots 0..7 of a fragment whose contraction runs
+// over those 32 tokens, so P and dS feed the next MFMA with no data movement
+// (acc_to_frag), and its partner operand is a plain frag_ch.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,14 +28,14 @@ namespace psa {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -39,115 +44,229 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
 
+template <typename T> constexpr bool is_bf16() { return sizeof(T) == 2; }
+
 // ---------------------------------------------------------------- fragments
 template <typename T> struct Frag;
 template <> struct Frag<float> { float v[8]; };
 template <> struct Frag<bf16> { bf16x8 v; };
 
-// c += a * b over one 32-wide contraction chunk; KS = slots carrying data
-// (8, or 4 when the contraction dimension ends 16 into the chunk).
-template <int KS>
 __device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
 }
-template <int KS>
 __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
 #pragma unroll
-  for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ Frag<T> ones_frag();
+template <> __device__ __forceinline__ Frag<bf16> ones_frag<bf16>() {
+  Frag<bf16> f;
+  f.v = bf16x8{(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> ones_frag<float>() {
+  Frag<float> f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f.v[s] = 1.f;
+  return f;
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// MFMA rows = tokens col0..col0+15 of the tile, contraction = tile rows
-// k0..k0+31 (channels).
-template <int KS>
-__device__ __forceinline__ void load_tr(Frag<bf16>& f, const bf16* tile, int ld, int k0, int col0) {
+// Token of row m (0..15) of score block h within a 32-token chunk.
+__device__ __forceinline__ int perm_row(int m, int h) { return 8 * (m >> 2) + 4 * h + (m & 3); }
+
+// Token-major tiles: element (token r, channel ch) lives at
+//   r * ldt + 32 * (r / 16) + ch,   ldt = channels + 8.
+// The odd pitch (in 16-byte units) separates 16 consecutive rows; the extra
+// 64-byte skew every 16 rows separates rows r and r + 16, which one permuted
+// fragment read (rows 8a + b + 4h) touches together.  With it, fragment reads
+// and the staging writes are free of LDS bank conflicts for every tile width.
+__device__ __forceinline__ int tm_off(int r, int ch, int ldt) { return r * ldt + 32 * (r >> 4) + ch; }
+constexpr int tm_elems(int rows, int ldt) { return rows * ldt + 32 * ((rows + 15) / 16); }
+
+// Rows = tokens row0 + (PERM ? perm_row(lane&15, h) : lane&15); contraction
+// over channels k0 .. k0+31 of a tensor with CV channels (CV % 16 == 0; the
+// upper half of a chunk past CV reads as zero).
+// bf16: token-major tile (see tm_off).  fp32: channel-major tile
+// nat[ch][token], pitch ldn.
+template <int CV, bool PERM>
+__device__ __forceinline__ void frag_tok(Frag<bf16>& f, const bf16* tm, int ldt, const bf16*, int, int row0,
+                                         int h, int k0) {
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  // Each 16-lane group reads a 4 (row) x 16 (token) block; lane t supplies
-  // the 4 tokens 4*(t%4).. of row t/4 and receives token t of all 4 rows.
-  const bf16* p = tile + (k0 + 4 * g + (t >> 2)) * ld + col0 + 4 * (t & 3);
-  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  i16x4 hi = {0, 0, 0, 0};
-  if constexpr (KS == 8) hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * ld));
-  i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  f.v = __builtin_bit_cast(bf16x8, r);
+  const int row = row0 + (PERM ? perm_row(t, h) : t);
+  if (CV % 32 == 0 || k0 + 8 * g < CV) {
+    f.v = *(const bf16x8*)(tm + tm_off(row, k0 + 8 * g, ldt));
+  } else {
+    f.v = bf16x8{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  }
 }
-template <int KS>
-__device__ __forceinline__ void load_tr(Frag<float>& f, const float* tile, int ld, int k0, int col0) {
+template <int CV, bool PERM>
+__device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, const float* nat, int ldn, int row0,
+                                         int h, int k0) {
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  const float* p = tile + (k0 + 4 * g) * ld + col0 + t;
+  const int tok = row0 + (PERM ? perm_row(t, h) : t);
+  const bool live = CV % 32 == 0 || k0 + 8 * g < CV;
+  const float* p = nat + (k0 + 8 * g) * ldn + tok;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = s < KS ? p[(16 * (s >> 2) + (s & 3)) * ld] : 0.f;
+  for (int s = 0; s < 8; ++s) f.v[s] = live ? p[s * ldn] : 0.f;
 }
 
-// MFMA rows = tile rows row0..row0+15 (channels), contraction = tokens
-// col0..col0+31.
-__device__ __forceinline__ void load_nat(Frag<bf16>& f, const bf16* tile, int ld, int row0, int col0) {
+// Rows = channels ch0 .. ch0+15, contraction over tokens tok0 + 8g .. +7.
+__device__ __forceinline__ void frag_ch(Frag<bf16>& f, const bf16* nat, int ldn, int ch0, int tok0) {
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  const bf16* p = tile + (row0 + t) * ld + col0 + 4 * g;
-  bf16x4 lo = *(const bf16x4*)p;
-  bf16x4 hi = *(const bf16x4*)(p + 16);
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  f.v = *(const bf16x8*)(nat + (ch0 + t) * ldn + tok0 + 8 * g);
 }
-__device__ __forceinline__ void load_nat(Frag<float>& f, const float* tile, int ld, int row0, int col0) {
+__device__ __forceinline__ void frag_ch(Frag<float>& f, const float* nat, int ldn, int ch0, int tok0) {
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  const float* p = tile + (row0 + t) * ld + col0 + 4 * g;
-  f32x4 lo = *(const f32x4*)p;
-  f32x4 hi = *(const f32x4*)(p + 16);
+  const float* p = nat + (ch0 + t) * ldn + tok0 + 8 * g;
+  const f32x4 lo = *(const f32x4*)p, hi = *(const f32x4*)(p + 4);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) { f.v[s] = lo[s]; f.v[4 + s] = hi[s]; }
+  for (int s = 0; s < 4; ++s) {
+    f.v[s] = lo[s];
+    f.v[4 + s] = hi[s];
+  }
 }
 
-// Two vertically stacked 16x16 accumulator blocks (rows 0-15 in a0, 16-31 in
-// a1) as a B operand whose contraction index is the accumulator row.
+// Score blocks h = 0, 1 of one 32-token chunk -> B operand over those tokens.
 __device__ __forceinline__ void acc_to_frag(Frag<bf16>& f, const f32x4& a0, const f32x4& a1) {
   f.v = bf16x8{(bf16)a0[0], (bf16)a0[1], (bf16)a0[2], (bf16)a0[3],
                (bf16)a1[0], (bf16)a1[1], (bf16)a1[2], (bf16)a1[3]};
 }
 __device__ __forceinline__ void acc_to_frag(Frag<float>& f, const f32x4& a0, const f32x4& a1) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) { f.v[s] = a0[s]; f.v[4 + s] = a1[s]; }
+  for (int s = 0; s < 4; ++s) {
+    f.v[s] = a0[s];
+    f.v[4 + s] = a1[s];
+  }
 }
 
-// ------------------------------------------------------------- tile loader
-// Rows [0, R) x tokens [j0, j0 + BC) of a channel-major slice (row stride N
-// elements) -> registers -> LDS tile [R][ld].  Tokens >= N read as zero.
-// VECOK: N is a multiple of the 16-byte vector width, so every 16-byte chunk
-// is aligned and either wholly inside or wholly past the row end.
-template <typename T, int R, int BC, int NT, bool VECOK>
-struct TileLoader {
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int CPR = BC / VEC;
-  static constexpr int CHUNKS = R * CPR;
-  static constexpr int PER = (CHUNKS + NT - 1) / NT;
-  static_assert(BC % VEC == 0, "tile width must be a whole number of 16-byte chunks");
-  uint4 reg[PER];
+// ------------------------------------------------------------------ staging
+// Pitches (elements): 16 bytes of padding per row keeps every row 16-byte
+// aligned and spreads the 16 rows one fragment read touches over all banks.
+template <typename T> constexpr int nat_pitch(int tokens) { return tokens + 16 / (int)sizeof(T); }
+constexpr int tm_pitch(int channels) { return channels + 8; }
 
-  __device__ __forceinline__ void load(const T* __restrict__ src, int N, int j0, int tid) {
+// Global -> registers -> LDS for a tile of C channel rows x BT tokens from
+// token j0 (tokens >= N read as zero).  Rows [0, SPLIT) come from src_lo and
+// rows [SPLIT, C) from src_hi, both channel-major with row stride N.
+//   bf16: each thread owns 4-channel x 8-token blocks (four 16-byte loads).
+//         Rows in [NAT_LO, NAT_HI) go to a channel-major tile
+//         nat[row - NAT_LO][nat_pitch(BT)]; rows in [0, TM_HI) are also
+//         transposed in registers into a token-major tile tm[token][row]
+//         (pitch tm_pitch(TM_HI)).
+//   fp32: 16-byte chunks (4 tokens of one row); all C rows go to the
+//         channel-major tile (token-major reads gather from it instead).
+// VECOK: N is a multiple of the 16-byte vector, so every chunk is aligned and
+// wholly inside or wholly past the row end.
+template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
+struct Stager;
+
+template <int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
+struct Stager<bf16, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
+  static constexpr int CG = C / 4, TC = BT / 8, NB = CG * TC, PER = (NB + NT - 1) / NT;
+  static constexpr int LDN = nat_pitch<bf16>(BT), LDT = tm_pitch(TM_HI);
+  static constexpr int NAT_ELEMS = (NAT_HI - NAT_LO) * LDN, TM_ELEMS = TM_HI > 0 ? tm_elems(BT, LDT) : 0;
+  // Block q: 4 consecutive blocks run along the tokens of one 4-row group
+  // (64 contiguous bytes per row in HBM), then the next row group.
+  static constexpr int TCL = TC < 4 ? TC : 4;
+  static_assert(TC % TCL == 0, "token chunks");
+  __device__ static __forceinline__ int blk_tc(int q) { return q % TCL + TCL * (q / (TCL * CG)); }
+  __device__ static __forceinline__ int blk_cg(int q) { return (q / TCL) % CG; }
+  static constexpr int NAT_BASE = NAT_LO;  // channel of the first natural row
+  static_assert(C % 4 == 0 && BT % 8 == 0 && SPLIT % 4 == 0 && TM_HI % 4 == 0 && NAT_LO % 4 == 0 &&
+                    NAT_HI % 4 == 0, "tile shape");
+  u32x4 r[PER][4];
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ lo, const bf16* __restrict__ hi, int N, int j0,
+                                       int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
-      reg[u] = make_uint4(0, 0, 0, 0);
-      if (CHUNKS % NT != 0 && q >= CHUNKS) continue;
-      const int row = q / CPR, j = j0 + (q - row * CPR) * VEC;
-      const T* p = src + (size_t)row * N + j;
-      if constexpr (VECOK) {
-        if (j < N) reg[u] = *(const uint4*)p;
-      } else {
-        T tmp[VEC];
+      const int tc = blk_tc(q), cg = blk_cg(q);
+      const int j = j0 + 8 * tc;
+      const bool live = NB % NT == 0 || q < NB;
+      const bf16* base = 4 * cg < SPLIT ? lo + (size_t)(4 * cg) * N : hi + (size_t)(4 * cg - SPLIT) * N;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) tmp[e] = (j + e < N) ? p[e] : (T)0.f;
-        __builtin_memcpy(&reg[u], tmp, 16);
+      for (int i = 0; i < 4; ++i) {
+        r[u][i] = u32x4{0u, 0u, 0u, 0u};
+        if (!live) continue;
+        const bf16* p = base + (size_t)i * N + j;
+        if constexpr (VECOK) {
+          if (j < N) r[u][i] = *(const u32x4*)p;
+        } else {
+          unsigned short tmp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tmp[e] = (j + e < N) ? ((const unsigned short*)p)[e] : (unsigned short)0;
+          __builtin_memcpy(&r[u][i], tmp, 16);
+        }
       }
     }
   }
-  __device__ __forceinline__ void store(T* tile, int ld, int tid) const {
+  __device__ __forceinline__ void store(bf16* nat, bf16* tm, int tid) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * NT;
+      if (NB % NT != 0 && q >= NB) continue;
+      const int tc = blk_tc(q), cg = blk_cg(q), row = 4 * cg;
+      if (NAT_HI > NAT_LO && row >= NAT_LO && row < NAT_HI) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4*)(nat + (row - NAT_LO + i) * LDN + 8 * tc) = r[u][i];
+      }
+      if (row < TM_HI) {
+        // token 8*tc + e receives rows row..row+3: halves e%2 of dword e/2.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = e >> 1;
+          unsigned w0, w1;
+          if (e & 1) {
+            w0 = (r[u][0][d] >> 16) | (r[u][1][d] & 0xffff0000u);
+            w1 = (r[u][2][d] >> 16) | (r[u][3][d] & 0xffff0000u);
+          } else {
+            w0 = (r[u][0][d] & 0xffffu) | (r[u][1][d] << 16);
+            w1 = (r[u][2][d] & 0xffffu) | (r[u][3][d] << 16);
+          }
+          *(u32x2*)(tm + tm_off(8 * tc + e, row, LDT)) = u32x2{w0, w1};
+        }
+      }
+    }
+  }
+};
+
+template <int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
+struct Stager<float, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
+  static constexpr int CPR = BT / 4, CHUNKS = C * CPR, PER = (CHUNKS + NT - 1) / NT;
+  static constexpr int LDN = nat_pitch<float>(BT), LDT = 0;
+  static constexpr int NAT_ELEMS = C * LDN, TM_ELEMS = 0;
+  static constexpr int NAT_BASE = 0;
+  static_assert(BT % 4 == 0, "tile shape");
+  f32x4 r[PER];
+
+  __device__ __forceinline__ void load(const float* __restrict__ lo, const float* __restrict__ hi, int N, int j0,
+                                       int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * NT;
+      r[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (CHUNKS % NT != 0 && q >= CHUNKS) continue;
+      const int row = q / CPR, j = j0 + (q - row * CPR) * 4;
+      const float* p = (row < SPLIT ? lo + (size_t)row * N : hi + (size_t)(row - SPLIT) * N) + j;
+      if constexpr (VECOK) {
+        if (j < N) r[u] = *(const f32x4*)p;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[u][e] = (j + e < N) ? p[e] : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* nat, float*, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
       if (CHUNKS % NT != 0 && q >= CHUNKS) continue;
       const int row = q / CPR, cc = q - row * CPR;
-      *(uint4*)(tile + row * ld + cc * VEC) = reg[u];
+      *(f32x4*)(nat + row * LDN + cc * 4) = r[u];
     }
   }
 };

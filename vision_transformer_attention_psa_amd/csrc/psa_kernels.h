@@ -7,15 +7,16 @@
 // summed with float atomics) is not used here.  Instead:
 //
 //   psa_fwd_kernel   one workgroup per (slice, tile of BM queries); each wave
-//                    keeps QW queries stationary and streams key tiles of BN
-//                    through LDS: S^T = K Q^T (MFMA), online softmax in
-//                    log2 units, O^T += V^T P^T (MFMA).  Writes O and LSE.
-//   psa_bwd_pre      D_i = sum_c dO_ic O_ic and LSE in log2 units, one
-//                    thread per query (coalesced over tokens).
-//   psa_bwd_dkdv     one workgroup per (slice, tile of keys); keys
-//                    stationary, query tiles streamed: S = Q K^T,
-//                    dP = dO V^T, P = exp(S - LSE), dS = P (dP - D),
-//                    dV^T += dO^T P, dK^T += Q^T dS.
+//                    keeps QW queries stationary in registers and streams key
+//                    tiles through LDS: S^T = K Q^T, online softmax in log2
+//                    units (rescale only when the running max grows by more
+//                    than 2^8), O^T += V^T P^T and the row sums l += 1 P^T,
+//                    all on MFMA.  Writes O and LSE.
+//   psa_bwd_pre      D_i = sum_c dO_ic O_ic and LSE in log2 units.
+//   psa_bwd_dkdv     one workgroup per (slice, tile of keys); keys stationary,
+//                    query tiles streamed: S = Q K^T, dP = dO V^T,
+//                    P = exp(S - LSE), dS = P (dP - D), dV^T += dO^T P,
+//                    dK^T += Q^T dS.
 //   psa_bwd_dq       one workgroup per (slice, tile of queries); queries
 //                    stationary, key tiles streamed: S^T, dP^T, dS^T as
 //                    above, dQ^T += K^T dS^T.
@@ -24,38 +25,40 @@
 //
 // Orientation: outputs are accumulated transposed (channels as MFMA rows,
 // tokens as MFMA columns) so that accumulator lanes run along tokens and
-// stores to the channel-major tensors are coalesced; the score matrix is
-// built as S^T where the next GEMM contracts over keys (fwd, dQ) and as S
-// where it contracts over queries (dK/dV), so that P and dS feed the next
-// MFMA straight from registers (acc_to_frag).
+// stores into the channel-major tensors are coalesced.  Scores are S^T where
+// the next GEMM contracts over keys (fwd, dQ) and S where it contracts over
+// queries (dK/dV); their rows are permuted within each 32-token chunk (see
+// psa_common.h) so that P and dS become the next MFMA operand in place.
 #pragma once
 #include "psa_common.h"
 
 namespace psa {
 
-constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kPosInf = __builtin_huge_valf();
+constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before a rescale
 
 template <int D> struct Chunks {
-  static constexpr int n = (D + 31) / 32;            // 32-wide contraction chunks
-  static constexpr int last = (D % 32 == 16) ? 4 : 8; // data slots in the last one
+  static constexpr int n = (D + 31) / 32;  // 32-wide contraction chunks
   static_assert(D % 16 == 0, "head dims must be multiples of 16");
 };
 
-template <typename T> constexpr int lds_pad() { return 16 / (int)sizeof(T); }
+template <typename T, typename S>
+__device__ __forceinline__ T* tm_of(T* base, const S&) { return base + S::NAT_ELEMS; }
 
 // =================================================================== forward
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
-__global__ __launch_bounds__(NW * 64) void psa_fwd_kernel(
-    const T* __restrict__ qkv, T* __restrict__ o, float* __restrict__ lse, int N, int n_qtiles,
-    float c /* scale * log2(e) */) {
+__global__ __launch_bounds__(NW * 64) void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
+                                                         float* __restrict__ lse, int N, int n_qtiles,
+                                                         float c /* scale * log2(e) */) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
-  constexpr int KC = Chunks<DK>::n, KSL = Chunks<DK>::last;
-  constexpr int MB = BN / 16;
-  constexpr int LDK = BN + lds_pad<T>(), LDQ = BM + lds_pad<T>();
-  constexpr int KV_ELEMS = (DK + DV) * LDK;
-  constexpr int SMEM = 2 * KV_ELEMS > DK * LDQ ? 2 * KV_ELEMS : DK * LDQ;
+  constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
+  // K|V tile: K rows token-major (bf16) for S^T, V rows channel-major for PV.
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK + DV, DK, DK, DK + DV>;
+  using SQ = Stager<T, DK, BM, NT, VECOK, DK, DK, 0, 0>;
+  constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
+  constexpr int QE = SQ::NAT_ELEMS + SQ::TM_ELEMS;
+  constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
+  constexpr int VROW = is_bf16<T>() ? 0 : DK;  // first V row in the channel-major tile
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -64,126 +67,125 @@ __global__ __launch_bounds__(NW * 64) void psa_fwd_kernel(
   const T* Qg = qkv + (size_t)bh * (2 * DK + DV) * N;
   const T* KVg = Qg + (size_t)DK * N;
 
-  // Stationary queries: B operand of S^T = K Q^T (lane = query, slots = channels).
+  // Stationary queries: B operands of S^T = K Q^T (lane = query column).
   Frag<T> qf[QB][KC];
   {
-    TileLoader<T, DK, BM, NT, VECOK> ql;
-    ql.load(Qg, N, i0, tid);
-    ql.store(smem, LDQ, tid);
+    SQ sq;
+    sq.load(Qg, Qg, N, i0, tid);
+    sq.store(smem, tm_of(smem, sq), tid);
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < QB; ++nb)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        if (kc == KC - 1) load_tr<KSL>(qf[nb][kc], smem, LDQ, 32 * kc, w * QW + 16 * nb);
-        else load_tr<8>(qf[nb][kc], smem, LDQ, 32 * kc, w * QW + 16 * nb);
-      }
+      for (int kc = 0; kc < KC; ++kc)
+        frag_tok<DK, false>(qf[nb][kc], tm_of(smem, sq), SQ::LDT, smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
     __syncthreads();
   }
 
-  TileLoader<T, DK + DV, BN, NT, VECOK> kvl;
-  kvl.load(KVg, N, 0, tid);
-  kvl.store(smem, LDK, tid);
+  SKV st;
+  st.load(KVg, KVg, N, 0, tid);
+  st.store(smem, tm_of(smem, st), tid);
   __syncthreads();
 
-  float m[QB], l[QB];
-  f32x4 oacc[DV / 16][QB];
+  const Frag<T> ones = ones_frag<T>();
+  float m[QB];
+  f32x4 oacc[DV / 16][QB], lacc[QB];
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
     m[nb] = kNegInf;
-    l[nb] = 0.f;
+    lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
-    const T* Kt = smem + (kt & 1) * KV_ELEMS;
-    const T* Vt = Kt + DK * LDK;
-    if (kt + 1 < nkt) kvl.load(KVg, N, (kt + 1) * BN, tid);
+    T* nat = smem + (kt & 1) * BUF;
+    const T* tm = tm_of(nat, st);
+    const T* Vt = nat + (VROW + 0) * SKV::LDN;
+    if (kt + 1 < nkt) st.load(KVg, KVg, N, (kt + 1) * BN, tid);
+    const int j0 = kt * BN;
 
-    f32x4 s[MB][QB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int c2 = 0; c2 < BN / 32; ++c2) {
+      f32x4 s[2][QB];
 #pragma unroll
-      for (int nb = 0; nb < QB; ++nb) s[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        Frag<T> a;
-        if (kc == KC - 1) {
-          load_tr<KSL>(a, Kt, LDK, 32 * kc, 16 * mb);
+        for (int nb = 0; nb < QB; ++nb) s[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int nb = 0; nb < QB; ++nb) mma<KSL>(s[mb][nb], a, qf[nb][kc]);
-        } else {
-          load_tr<8>(a, Kt, LDK, 32 * kc, 16 * mb);
+        for (int kc = 0; kc < KC; ++kc) {
+          Frag<T> a;
+          frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
-          for (int nb = 0; nb < QB; ++nb) mma<8>(s[mb][nb], a, qf[nb][kc]);
+          for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
       }
-    }
-    const int j0 = kt * BN;
-    if (j0 + BN > N) {  // keys past the end of the sequence get zero weight
+      if (j0 + 32 * c2 + 32 > N) {  // keys past the end get zero weight
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (j0 + 16 * mb + 4 * g + r >= N)
+          for (int r = 0; r < 4; ++r)
+            if (j0 + 32 * c2 + 8 * g + 4 * h + r >= N)
 #pragma unroll
-            for (int nb = 0; nb < QB; ++nb) s[mb][nb][r] = kNegInf;
-    }
+              for (int nb = 0; nb < QB; ++nb) s[h][nb][r] = kNegInf;
+      }
 
-    // Online softmax per query column (this lane's column, rows over 4 lane groups).
+      // Online softmax per query column; the 4 lane groups hold the rows.
+      float mt[QB];
+      bool grow = false;
 #pragma unroll
-    for (int nb = 0; nb < QB; ++nb) {
-      float mx = s[0][nb][0];
+      for (int nb = 0; nb < QB; ++nb) {
+        float mx = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mt[nb] = mx * c;
+        grow |= mt[nb] > m[nb] + kRescaleSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int nb = 0; nb < QB; ++nb) {
+          const float mn = fmaxf(m[nb], mt[nb]);
+          const float alpha = fast_exp2(m[nb] - mn);
+          m[nb] = mn;
+          lacc[nb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[mb][nb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[nb], mx * c);
-      const float alpha = fast_exp2(m[nb] - mnew);
-      m[nb] = mnew;
-      float ls = l[nb] * alpha;
-#pragma unroll
-      for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[mb][nb][r], c, -mnew));
-          s[mb][nb][r] = p;
-          ls += p;
+          for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] *= alpha;
         }
-      l[nb] = ls;
-    }
-
-    // O^T += V^T P^T, contraction over this tile's keys.
-#pragma unroll
-    for (int kc2 = 0; kc2 < MB / 2; ++kc2) {
+      }
       Frag<T> pf[QB];
 #pragma unroll
-      for (int nb = 0; nb < QB; ++nb) acc_to_frag(pf[nb], s[2 * kc2][nb], s[2 * kc2 + 1][nb]);
+      for (int nb = 0; nb < QB; ++nb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[h][nb][r] = fast_exp2(__builtin_fmaf(s[h][nb][r], c, -m[nb]));
+        acc_to_frag(pf[nb], s[0][nb], s[1][nb]);
+        mma(lacc[nb], ones, pf[nb]);
+      }
+      // O^T += V^T P^T over this chunk's 32 keys.
 #pragma unroll
       for (int cb = 0; cb < DV / 16; ++cb) {
         Frag<T> a;
-        load_nat(a, Vt, LDK, 16 * cb, 32 * kc2);
+        frag_ch(a, Vt, SKV::LDN, 16 * cb, 32 * c2);
 #pragma unroll
-        for (int nb = 0; nb < QB; ++nb) mma<8>(oacc[cb][nb], a, pf[nb]);
+        for (int nb = 0; nb < QB; ++nb) mma(oacc[cb][nb], a, pf[nb]);
       }
     }
 
-    if (kt + 1 < nkt) kvl.store(smem + ((kt + 1) & 1) * KV_ELEMS, LDK, tid);
+    if (kt + 1 < nkt) {
+      T* nx = smem + ((kt + 1) & 1) * BUF;
+      st.store(nx, tm_of(nx, st), tid);
+    }
     __syncthreads();
   }
 
-  // Epilogue: O = O_acc / l, LSE = ln(sum_j exp(S_ij)) = (m + log2 l) * ln 2.
+  // Epilogue: every row of the ones-product holds the column sum l.
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
-    float lt = l[nb] + __shfl_xor(l[nb], 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = fast_rcp(lt);
+    const float l = lacc[nb][0];
+    const float inv = fast_rcp(l);
     const int i = i0 + w * QW + 16 * nb + t;
     if (i < N) {
 #pragma unroll
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void psa_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           o[((size_t)bh * DV + 16 * cb + 4 * g + r) * N + i] = from_f32<T>(oacc[cb][nb][r] * inv);
-      if (g == 0) lse[(size_t)bh * N + i] = (m[nb] + fast_log2(lt)) * kLn2;
+      if (g == 0) lse[(size_t)bh * N + i] = (m[nb] + fast_log2(l)) * kLn2;
     }
   }
 }
@@ -213,31 +215,24 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
   stats[idx] = make_float2(lse[idx] * kLog2e, d);
 }
 
-// Per-query statistics of one query tile staged beside the Q/dO tile.
-// Queries past the end get LSE = +inf (so P = 0) and D = 0.
-template <int BMQ, int NT>
-__device__ __forceinline__ void load_stats(float2* dst, const float2* __restrict__ src, int N, int q0, int tid) {
-  for (int q = tid; q < BMQ; q += NT) dst[q] = (q0 + q < N) ? src[q0 + q] : make_float2(kPosInf, 0.f);
-}
-
 // ============================================================ backward dK/dV
 template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
 __global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
     T* __restrict__ dpk, int N, int n_ktiles, float c, float scale) {
   constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
-  constexpr int KC = Chunks<DK>::n, KSL = Chunks<DK>::last;
-  constexpr int CC = Chunks<DV>::n, CSL = Chunks<DV>::last;
-  constexpr int MBQ = BMQ / 16;
-  constexpr int LDQ = BMQ + lds_pad<T>(), LDK = BNK + lds_pad<T>();
-  constexpr int QD_ELEMS = (DK + DV) * LDQ;
-  constexpr int QD_BYTES = 2 * QD_ELEMS * (int)sizeof(T) + 2 * BMQ * (int)sizeof(float2);
-  constexpr int KV_BYTES = (DK + DV) * LDK * (int)sizeof(T);
-  constexpr int SMEM = QD_BYTES > KV_BYTES ? QD_BYTES : KV_BYTES;
+  constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BMQ % 32 == 0, "query tile must be a multiple of 32");
+  // Q|dO tile: both layouts of every row.  K|V stationary tile: token-major.
+  using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, DK + DV, 0, DK + DV>;
+  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK + DV, DK + DV, 0, 0>;
+  constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 2 * BMQ * (int)sizeof(float2);
+  constexpr int KV_BYTES = (SKV::NAT_ELEMS + SKV::TM_ELEMS) * (int)sizeof(T);
+  constexpr int SMEM = QG_BYTES > KV_BYTES ? QG_BYTES : KV_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM];
   T* smem = (T*)smem_raw;
-  float2* sstats = (float2*)(smem_raw + 2 * QD_ELEMS * sizeof(T));
+  float2* sstats = (float2*)(smem_raw + 2 * TILE * sizeof(T));
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -251,22 +246,19 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
   // Stationary keys: B operands of S = Q K^T and dP = dO V^T (lane = key).
   Frag<T> kf[KB][KC], vf[KB][CC];
   {
-    TileLoader<T, DK + DV, BNK, NT, VECOK> kvl;
-    kvl.load(KVg, N, j0, tid);
-    kvl.store(smem, LDK, tid);
+    SKV sk;
+    sk.load(KVg, KVg, N, j0, tid);
+    sk.store(smem, tm_of(smem, sk), tid);
     __syncthreads();
+    const T* tm = tm_of(smem, sk);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      const int row0 = w * KW + 16 * kb;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        if (kc == KC - 1) load_tr<KSL>(kf[kb][kc], smem, LDK, 32 * kc, w * KW + 16 * kb);
-        else load_tr<8>(kf[kb][kc], smem, LDK, 32 * kc, w * KW + 16 * kb);
-      }
+      for (int kc = 0; kc < KC; ++kc) frag_tok<DK, false>(kf[kb][kc], tm, SKV::LDT, smem, SKV::LDN, row0, 0, 32 * kc);
 #pragma unroll
-      for (int cc = 0; cc < CC; ++cc) {
-        if (cc == CC - 1) load_tr<CSL>(vf[kb][cc], smem, LDK, DK + 32 * cc, w * KW + 16 * kb);
-        else load_tr<8>(vf[kb][cc], smem, LDK, DK + 32 * cc, w * KW + 16 * kb);
-      }
+      for (int cc = 0; cc < CC; ++cc)
+        frag_tok<DV, false>(vf[kb][cc], tm + DK, SKV::LDT, smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
     }
     __syncthreads();
   }
@@ -280,103 +272,85 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
     for (int db = 0; db < DK / 16; ++db) dkacc[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  TileLoader<T, DK, BMQ, NT, VECOK> ql;
-  TileLoader<T, DV, BMQ, NT, VECOK> gl;
-  ql.load(Qg, N, 0, tid);
-  gl.load(dOg, N, 0, tid);
-  ql.store(smem, LDQ, tid);
-  gl.store(smem + DK * LDQ, LDQ, tid);
-  load_stats<BMQ, NT>(sstats, st, N, 0, tid);
+  SQG sg;
+  sg.load(Qg, dOg, N, 0, tid);
+  sg.store(smem, tm_of(smem, sg), tid);
+  for (int q = tid; q < BMQ; q += NT) sstats[q] = q < N ? st[q] : make_float2(kPosInf, 0.f);
   __syncthreads();
 
   const int nqt = (N + BMQ - 1) / BMQ;
   for (int qt = 0; qt < nqt; ++qt) {
     const int cur = qt & 1;
-    const T* Qt = smem + cur * QD_ELEMS;
-    const T* Gt = Qt + DK * LDQ;
+    const T* nat = smem + cur * TILE;   // rows: Q channels, then dO channels
+    const T* tm = tm_of(nat, sg);       // columns: Q channels, then dO channels
     const float2* sq = sstats + cur * BMQ;
-    if (qt + 1 < nqt) {
-      ql.load(Qg, N, (qt + 1) * BMQ, tid);
-      gl.load(dOg, N, (qt + 1) * BMQ, tid);
-    }
+    if (qt + 1 < nqt) sg.load(Qg, dOg, N, (qt + 1) * BMQ, tid);
 
-    f32x4 s[MBQ][KB], dp[MBQ][KB];
 #pragma unroll
-    for (int mb = 0; mb < MBQ; ++mb) {
+    for (int c2 = 0; c2 < BMQ / 32; ++c2) {
+      f32x4 s[2][KB], dp[2][KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        Frag<T> a;
-        if (kc == KC - 1) {
-          load_tr<KSL>(a, Qt, LDQ, 32 * kc, 16 * mb);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mma<KSL>(s[mb][kb], a, kf[kb][kc]);
-        } else {
-          load_tr<8>(a, Qt, LDQ, 32 * kc, 16 * mb);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mma<8>(s[mb][kb], a, kf[kb][kc]);
-        }
-      }
-#pragma unroll
-      for (int cc = 0; cc < CC; ++cc) {
-        Frag<T> a;
-        if (cc == CC - 1) {
-          load_tr<CSL>(a, Gt, LDQ, 32 * cc, 16 * mb);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mma<CSL>(dp[mb][kb], a, vf[kb][cc]);
-        } else {
-          load_tr<8>(a, Gt, LDQ, 32 * cc, 16 * mb);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) mma<8>(dp[mb][kb], a, vf[kb][cc]);
-        }
-      }
-      // rows of this block: queries 16*mb + 4*g + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float2 q = sq[16 * mb + 4 * g + r];
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const float p = fast_exp2(__builtin_fmaf(s[mb][kb][r], c, -q.x));
-          s[mb][kb][r] = p;
-          dp[mb][kb][r] = p * (dp[mb][kb][r] - q.y);
+          s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          Frag<T> a;
+          frag_tok<DK, true>(a, tm, SQG::LDT, nat, SQG::LDN, 32 * c2, h, 32 * kc);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) mma(s[h][kb], a, kf[kb][kc]);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CC; ++cc) {
+          Frag<T> a;
+          frag_tok<DV, true>(a, tm + DK, SQG::LDT, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) mma(dp[h][kb], a, vf[kb][cc]);
+        }
+        // rows of block h: queries 32*c2 + 8g + 4h + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float2 q = sq[32 * c2 + 8 * g + 4 * h + r];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const float p = fast_exp2(__builtin_fmaf(s[h][kb][r], c, -q.x));
+            s[h][kb][r] = p;
+            dp[h][kb][r] = p * (dp[h][kb][r] - q.y);
+          }
         }
       }
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS, contraction over this tile's queries.
-#pragma unroll
-    for (int qc = 0; qc < MBQ / 2; ++qc) {
+      // dV^T += dO^T P and dK^T += Q^T dS over this chunk's 32 queries.
       Frag<T> pf[KB], dsf[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        acc_to_frag(pf[kb], s[2 * qc][kb], s[2 * qc + 1][kb]);
-        acc_to_frag(dsf[kb], dp[2 * qc][kb], dp[2 * qc + 1][kb]);
+        acc_to_frag(pf[kb], s[0][kb], s[1][kb]);
+        acc_to_frag(dsf[kb], dp[0][kb], dp[1][kb]);
       }
 #pragma unroll
       for (int cb = 0; cb < DV / 16; ++cb) {
         Frag<T> a;
-        load_nat(a, Gt, LDQ, 16 * cb, 32 * qc);
+        frag_ch(a, nat, SQG::LDN, DK + 16 * cb, 32 * c2);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma<8>(dvacc[cb][kb], a, pf[kb]);
+        for (int kb = 0; kb < KB; ++kb) mma(dvacc[cb][kb], a, pf[kb]);
       }
 #pragma unroll
       for (int db = 0; db < DK / 16; ++db) {
         Frag<T> a;
-        load_nat(a, Qt, LDQ, 16 * db, 32 * qc);
+        frag_ch(a, nat, SQG::LDN, 16 * db, 32 * c2);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) mma<8>(dkacc[db][kb], a, dsf[kb]);
+        for (int kb = 0; kb < KB; ++kb) mma(dkacc[db][kb], a, dsf[kb]);
       }
     }
 
     if (qt + 1 < nqt) {
-      T* nq = smem + (cur ^ 1) * QD_ELEMS;
-      ql.store(nq, LDQ, tid);
-      gl.store(nq + DK * LDQ, LDQ, tid);
-      load_stats<BMQ, NT>(sstats + (cur ^ 1) * BMQ, st, N, (qt + 1) * BMQ, tid);
+      T* nx = smem + (cur ^ 1) * TILE;
+      sg.store(nx, tm_of(nx, sg), tid);
+      const int q0 = (qt + 1) * BMQ;
+      for (int q = tid; q < BMQ; q += NT)
+        sstats[(cur ^ 1) * BMQ + q] = q0 + q < N ? st[q0 + q] : make_float2(kPosInf, 0.f);
     }
     __syncthreads();
   }
@@ -404,13 +378,15 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
     T* __restrict__ dpk, int N, int n_qtiles, float c, float scale) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
-  constexpr int KC = Chunks<DK>::n, KSL = Chunks<DK>::last;
-  constexpr int CC = Chunks<DV>::n, CSL = Chunks<DV>::last;
-  constexpr int MB = BN / 16;
-  constexpr int LDK = BN + lds_pad<T>(), LDQ = BM + lds_pad<T>();
-  constexpr int KV_ELEMS = (DK + DV) * LDK;
-  constexpr int SMEM = 2 * KV_ELEMS > (DK + DV) * LDQ ? 2 * KV_ELEMS : (DK + DV) * LDQ;
+  constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
+  // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T).
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK + DV, DK + DV, 0, DK>;
+  // Stationary Q|dO tile, token-major.
+  using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, DK + DV, 0, 0>;
+  constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
+  constexpr int QE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -425,27 +401,20 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
   Frag<T> qf[QB][KC], gf[QB][CC];
   float lse2[QB], dd[QB];
   {
-    TileLoader<T, DK, BM, NT, VECOK> ql;
-    TileLoader<T, DV, BM, NT, VECOK> gl;
-    ql.load(Qg, N, i0, tid);
-    gl.load(dOg, N, i0, tid);
-    ql.store(smem, LDQ, tid);
-    gl.store(smem + DK * LDQ, LDQ, tid);
+    SQG sq;
+    sq.load(Qg, dOg, N, i0, tid);
+    sq.store(smem, tm_of(smem, sq), tid);
     __syncthreads();
+    const T* tm = tm_of(smem, sq);
 #pragma unroll
     for (int nb = 0; nb < QB; ++nb) {
-      const int col = w * QW + 16 * nb;
+      const int row0 = w * QW + 16 * nb;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        if (kc == KC - 1) load_tr<KSL>(qf[nb][kc], smem, LDQ, 32 * kc, col);
-        else load_tr<8>(qf[nb][kc], smem, LDQ, 32 * kc, col);
-      }
+      for (int kc = 0; kc < KC; ++kc) frag_tok<DK, false>(qf[nb][kc], tm, SQG::LDT, smem, SQG::LDN, row0, 0, 32 * kc);
 #pragma unroll
-      for (int cc = 0; cc < CC; ++cc) {
-        if (cc == CC - 1) load_tr<CSL>(gf[nb][cc], smem, LDQ, DK + 32 * cc, col);
-        else load_tr<8>(gf[nb][cc], smem, LDQ, DK + 32 * cc, col);
-      }
-      const int i = i0 + col + t;
+      for (int cc = 0; cc < CC; ++cc)
+        frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
+      const int i = i0 + row0 + t;
       const float2 q = (i < N) ? stats[(size_t)bh * N + i] : make_float2(kPosInf, 0.f);
       lse2[nb] = q.x;
       dd[nb] = q.y;
@@ -459,80 +428,70 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
 #pragma unroll
     for (int db = 0; db < DK / 16; ++db) dqacc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  TileLoader<T, DK + DV, BN, NT, VECOK> kvl;
-  kvl.load(KVg, N, 0, tid);
-  kvl.store(smem, LDK, tid);
+  SKV sk;
+  sk.load(KVg, KVg, N, 0, tid);
+  sk.store(smem, tm_of(smem, sk), tid);
   __syncthreads();
 
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
-    const T* Kt = smem + (kt & 1) * KV_ELEMS;
-    const T* Vt = Kt + DK * LDK;
-    if (kt + 1 < nkt) kvl.load(KVg, N, (kt + 1) * BN, tid);
+    const T* nat = smem + (kt & 1) * BUF;  // K channel-major (fp32: K then V)
+    const T* tm = tm_of(nat, sk);          // K then V channels, token-major
+    if (kt + 1 < nkt) sk.load(KVg, KVg, N, (kt + 1) * BN, tid);
     const int j0 = kt * BN;
 
-    f32x4 s[MB][QB], dp[MB][QB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int c2 = 0; c2 < BN / 32; ++c2) {
+      const bool tail = j0 + 32 * c2 + 32 > N;
+      f32x4 s[2][QB], dp[2][QB];
 #pragma unroll
-      for (int nb = 0; nb < QB; ++nb) {
-        s[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        Frag<T> a;
-        if (kc == KC - 1) {
-          load_tr<KSL>(a, Kt, LDK, 32 * kc, 16 * mb);
-#pragma unroll
-          for (int nb = 0; nb < QB; ++nb) mma<KSL>(s[mb][nb], a, qf[nb][kc]);
-        } else {
-          load_tr<8>(a, Kt, LDK, 32 * kc, 16 * mb);
-#pragma unroll
-          for (int nb = 0; nb < QB; ++nb) mma<8>(s[mb][nb], a, qf[nb][kc]);
-        }
-      }
-#pragma unroll
-      for (int cc = 0; cc < CC; ++cc) {
-        Frag<T> a;
-        if (cc == CC - 1) {
-          load_tr<CSL>(a, Vt, LDK, 32 * cc, 16 * mb);
-#pragma unroll
-          for (int nb = 0; nb < QB; ++nb) mma<CSL>(dp[mb][nb], a, gf[nb][cc]);
-        } else {
-          load_tr<8>(a, Vt, LDK, 32 * cc, 16 * mb);
-#pragma unroll
-          for (int nb = 0; nb < QB; ++nb) mma<8>(dp[mb][nb], a, gf[nb][cc]);
-        }
-      }
-      const bool tail = j0 + BN > N;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool dead = tail && (j0 + 16 * mb + 4 * g + r >= N);
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) {
-          const float p = dead ? 0.f : fast_exp2(__builtin_fmaf(s[mb][nb][r], c, -lse2[nb]));
-          dp[mb][nb][r] = p * (dp[mb][nb][r] - dd[nb]);
+          s[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          Frag<T> a;
+          frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+#pragma unroll
+          for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CC; ++cc) {
+          Frag<T> a;
+          frag_tok<DV, true>(a, tm + DK, SKV::LDT, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
+#pragma unroll
+          for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool dead = tail && (j0 + 32 * c2 + 8 * g + 4 * h + r >= N);
+#pragma unroll
+          for (int nb = 0; nb < QB; ++nb) {
+            const float p = dead ? 0.f : fast_exp2(__builtin_fmaf(s[h][nb][r], c, -lse2[nb]));
+            dp[h][nb][r] = p * (dp[h][nb][r] - dd[nb]);
+          }
         }
       }
-    }
-
-    // dQ^T += K^T dS^T, contraction over this tile's keys.
-#pragma unroll
-    for (int kc2 = 0; kc2 < MB / 2; ++kc2) {
+      // dQ^T += K^T dS^T over this chunk's 32 keys.
       Frag<T> dsf[QB];
 #pragma unroll
-      for (int nb = 0; nb < QB; ++nb) acc_to_frag(dsf[nb], dp[2 * kc2][nb], dp[2 * kc2 + 1][nb]);
+      for (int nb = 0; nb < QB; ++nb) acc_to_frag(dsf[nb], dp[0][nb], dp[1][nb]);
 #pragma unroll
       for (int db = 0; db < DK / 16; ++db) {
         Frag<T> a;
-        load_nat(a, Kt, LDK, 16 * db, 32 * kc2);
+        frag_ch(a, nat, SKV::LDN, 16 * db, 32 * c2);
 #pragma unroll
-        for (int nb = 0; nb < QB; ++nb) mma<8>(dqacc[db][nb], a, dsf[nb]);
+        for (int nb = 0; nb < QB; ++nb) mma(dqacc[db][nb], a, dsf[nb]);
       }
     }
 
-    if (kt + 1 < nkt) kvl.store(smem + ((kt + 1) & 1) * KV_ELEMS, LDK, tid);
+    if (kt + 1 < nkt) {
+      T* nx = smem + ((kt + 1) & 1) * BUF;
+      sk.store(nx, tm_of(nx, sk), tid);
+    }
     __syncthreads();
   }
 
