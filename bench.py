@@ -17,8 +17,8 @@ inputs.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -40,7 +40,7 @@ def flops(wl) -> dict:
     return {
         "fwd": n2 * (wl.dk + wl.dv),                 # S = QK^T, O = PV
         "bwd": n2 * (3 * wl.dk + 2 * wl.dv),         # S recompute, dP, dV, dK, dQ
-        "fwd_dkdv": n2 * (2 * wl.dk + 2 * wl.dv),    # kernel: S, dP, dV, dK
+        "bwd_dkdv": n2 * (2 * wl.dk + 2 * wl.dv),    # kernel: S, dP, dV, dK
         "bwd_dq": n2 * (2 * wl.dk + wl.dv),          # kernel: S, dP, dQ (S, dP recomputed)
     }
 
@@ -53,6 +53,45 @@ def hbm_bytes(wl, e: int) -> dict:
         "bwd": BH * (e * N * (2 * (2 * dk + dv) + 2 * dv) + 4 * N),
         "bwd_pre": BH * (2 * e * N * dv + 4 * N + 8 * N),
     }
+
+
+KERNEL_SOURCES = ("psa_kernels.h", "psa_common.h", "psa_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_fingerprint() -> str:
+    """Hash of the HIP sources: counter-based traffic is reported only while it
+    was measured on exactly these kernels."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "vision_transformer_attention_psa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Measured HBM bytes per launch {kernel: bytes} for `workload`, or None
+    when absent or taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("fingerprint") != kernel_fingerprint():
+        return None
+    return rec.get("workloads", {}).get(workload)
+
+
+def copy_calibration(torch, mib: int) -> None:
+    """One elementwise pass dst = src * 1 over `mib` MiB of float32 (a kernel of
+    known HBM traffic: mib MiB read, mib MiB written, far larger than the
+    caches) used to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def device_inputs(torch, x):
@@ -121,14 +160,15 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
 def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
-    per_launch = {"fwd": fl["fwd"], "bwd_dkdv": fl["fwd_dkdv"], "bwd_dq": fl["bwd_dq"]}
+    per_launch = {"fwd": fl["fwd"], "bwd_dkdv": fl["bwd_dkdv"], "bwd_dq": fl["bwd_dq"]}
     us = r["kernel_avg_us"]
     name = max(per_launch, key=lambda k: us[k])
     achieved = per_launch[name] / (us[name] * 1e-6) / 1e12
     return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": r["peak_tflops"],
             "unit": "TFLOP/s", "frac": achieved / r["peak_tflops"], "avg_us": us[name],
             "flops_per_launch": per_launch[name],
-            "traffic": (traffic or {}).get(name)}
+            "traffic": (traffic or {}).get(name),
+            "traffic_unit": "bytes/launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
 
 
 def cpu_baseline(wl, budget_s: float) -> dict:
@@ -172,8 +212,8 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--also", default=",".join(ALSO), help="comma list of extra workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
-    ap.add_argument("--traffic-json", default=None,
-                    help="per-kernel HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one plain MIB-MiB device copy first (reference kernel for counter scaling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -189,6 +229,8 @@ def main() -> int:
         print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
     wl = inputs.WORKLOADS[args.workload]
     print(f"[bench] {wl.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
     r = time_workload(torch, wl, args.steps, args.warmup)
@@ -201,10 +243,7 @@ def main() -> int:
                                         "fwd_bwd_tflops", "fwd_bwd_pct_mfma_peak", "kernel_avg_us")}
         print(f"[bench] {name}: fwd {a['fwd_us']:.1f} us, bwd {a['bwd_us']:.1f} us, "
               f"bwd {a['bwd_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    traffic = None
-    if args.traffic_json and os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            traffic = json.load(f).get(wl.name)
+    traffic = load_traffic(wl.name)
     cpu = None
     if args.cpu_budget > 0:
         print(f"[bench] cpu baseline: oracle on {wl.name} slices (~{args.cpu_budget:.0f} s)",

@@ -37,7 +37,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("PSA_ATTN_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with vision_transformer_attention_psa_amd.build "
                            "(or __graft_entry__.build()) before use")

@@ -39,10 +39,12 @@ def sources() -> list[str]:
     return [os.path.join(CSRC, "psa_attn.hip")]
 
 
-def build_library(verbose: bool = False, extra: list[str] | None = None) -> str:
+def build_library(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
     """Compile the HIP kernels and the C ABI into libpsa_attn.so (always
-    recompiles).  Returns the library path."""
-    tmp = LIB_PATH + ".tmp"
+    recompiles).  `extra` appends compiler flags (e.g. tile overrides) and
+    `out` redirects the output path.  Returns the library path."""
+    target = out or LIB_PATH
+    tmp = target + ".tmp"
     cmd = [hipcc(), f"--offload-arch={OFFLOAD_ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-command-line-argument", *DEVICE_FLAGS,
            f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp, *(extra or [])]
@@ -57,8 +59,8 @@ def build_library(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

@@ -27,10 +27,32 @@ int fail(int code, const std::string& msg) {
 // Tile shapes per element type.  bf16 fragments take half the registers of
 // fp32 ones, so bf16 tiles are twice as wide in the stationary dimension.
 template <typename T> struct Tiles;
+// Defaults can be overridden at build time (-DPSA_BF16_FWD_QB=...) for tuning.
+#ifndef PSA_BF16_FWD_QB
+#define PSA_BF16_FWD_QB 4
+#endif
+#ifndef PSA_BF16_FWD_NW
+#define PSA_BF16_FWD_NW 4
+#endif
+#ifndef PSA_BF16_DKDV_KB
+#define PSA_BF16_DKDV_KB 2
+#endif
+#ifndef PSA_BF16_DKDV_NW
+#define PSA_BF16_DKDV_NW 4
+#endif
+#ifndef PSA_BF16_DKDV_BMQ
+#define PSA_BF16_DKDV_BMQ 64
+#endif
+#ifndef PSA_BF16_DQ_QB
+#define PSA_BF16_DQ_QB 2
+#endif
+#ifndef PSA_BF16_DQ_NW
+#define PSA_BF16_DQ_NW 4
+#endif
 template <> struct Tiles<psa::bf16> {
-  static constexpr int FWD_NW = 4, FWD_QB = 4, FWD_BN = 64;
-  static constexpr int DKDV_NW = 4, DKDV_KB = 2, DKDV_BMQ = 64;
-  static constexpr int DQ_NW = 4, DQ_QB = 4, DQ_BN = 64;
+  static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = PSA_BF16_FWD_QB, FWD_BN = 64;
+  static constexpr int DKDV_NW = PSA_BF16_DKDV_NW, DKDV_KB = PSA_BF16_DKDV_KB, DKDV_BMQ = PSA_BF16_DKDV_BMQ;
+  static constexpr int DQ_NW = PSA_BF16_DQ_NW, DQ_QB = PSA_BF16_DQ_QB, DQ_BN = 64;
 };
 template <> struct Tiles<float> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;

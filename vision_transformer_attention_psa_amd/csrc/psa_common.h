@@ -129,6 +129,23 @@ __device__ __forceinline__ void frag_ch(Frag<float>& f, const float* nat, int ld
   }
 }
 
+// Empty asm that consumes a fragment: marks it live at this point so that the
+// code computing it is not moved below later control flow.
+__device__ __forceinline__ void pin(const Frag<bf16>& f) { asm volatile("" ::"v"(f.v)); }
+__device__ __forceinline__ void pin(const Frag<float>& f) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(f.v[s]));
+}
+
+// Max over the four lanes l, l^16, l^32, l^48 (the four row groups holding
+// one accumulator column), with the gfx950 row-swap permutes: no LDS trip.
+__device__ __forceinline__ float wave_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Score blocks h = 0, 1 of one 32-token chunk -> B operand over those tokens.
 __device__ __forceinline__ void acc_to_frag(Frag<bf16>& f, const f32x4& a0, const f32x4& a1) {
   f.v = bf16x8{(bf16)a0[0], (bf16)a0[1], (bf16)a0[2], (bf16)a0[3],

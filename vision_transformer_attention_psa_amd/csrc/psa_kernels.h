@@ -138,9 +138,7 @@ __global__ __launch_bounds__(NW * 64) void psa_fwd_kernel(const T* __restrict__ 
       for (int nb = 0; nb < QB; ++nb) {
         float mx = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
         mx = fmaxf(mx, fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mt[nb] = mx * c;
+        mt[nb] = wave_max4(mx) * c;
         grow |= mt[nb] > m[nb] + kRescaleSlack;
       }
       if (__builtin_amdgcn_ballot_w64(grow)) {

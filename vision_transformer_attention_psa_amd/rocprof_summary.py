@@ -1,0 +1,131 @@
+"""Summaries of rocprofv3 CSV output for the profiles/ directory.
+
+  stats   <kernel_stats.csv> <out.md> --command "..."
+          per-kernel call count / total / average / min / max duration
+  traffic <fetch counter_collection.csv> <write counter_collection.csv>
+          --workload NAME --copy-mib M --out-json profiles/traffic.json
+          --out-md profiles/<...>.md --command "..."
+          HBM bytes per launch of each PSA kernel from FETCH_SIZE and
+          WRITE_SIZE, scaled by what the same counters read for the
+          calibration pass (dst = src * 1 over M MiB of float32: M MiB read,
+          M MiB written).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
+             ("psa_bwd_dkdv_kernel", "bwd_dkdv"), ("psa_bwd_dq_kernel", "bwd_dq"))
+
+
+def short_name(kernel: str) -> str:
+    for pat, slot in PSA_SLOTS:
+        if pat in kernel:
+            m = re.search(r"I(DF16b|f)(?:Li(\d+)E)?(?:Li(\d+)E)?", kernel)
+            if m:
+                dt = "bf16" if m.group(1) == "DF16b" else "f32"
+                dims = "x".join(d for d in m.groups()[1:] if d)
+                return f"{slot}<{dt},{dims}>"
+            return slot
+    return kernel[:60]
+
+
+def stats(path: str, out: str, command: str) -> None:
+    rows = list(csv.DictReader(open(path)))
+    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+             "| kernel | calls | total us | avg us | min us | max us | % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        ns = lambda k: float(r[k]) / 1000.0
+        lines.append(f"| {short_name(name)} | {r['Calls']} | {ns('TotalDurationNs'):.1f} | "
+                     f"{ns('AverageNs'):.1f} | {ns('MinNs'):.1f} | {ns('MaxNs'):.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def per_dispatch(path: str, counter: str) -> dict:
+    """{kernel name: [value per dispatch]} for one counter."""
+    acc = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in acc.items()}
+
+
+def traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, out_json: str,
+            out_md: str, command: str, fingerprint: str) -> None:
+    f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = per_dispatch(write_csv, "WRITE_SIZE")
+    calib = [k for k in f if "MulFunctor" in k]
+    if not calib:
+        sys.exit("no calibration kernel (MulFunctor) in the FETCH_SIZE run")
+    known = copy_mib * float(1 << 20)
+    f_cal = max(f[calib[0]])
+    w_cal = max(w[[k for k in w if "MulFunctor" in k][0]])
+    f_scale, w_scale = known / f_cal, known / w_cal
+    res, lines = {}, []
+    for k in f:
+        slot = next((s for p, s in PSA_SLOTS if p in k), None)
+        if slot is None:
+            continue
+        fb = sum(f[k]) / len(f[k]) * f_scale
+        wb = sum(w.get(k, [0.0])) / max(1, len(w.get(k, []))) * w_scale
+        res[slot] = fb + wb
+        lines.append(f"| {short_name(k)} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} |")
+    rec = {}
+    if os.path.exists(out_json):
+        rec = json.load(open(out_json))
+    if rec.get("fingerprint") != fingerprint:
+        rec = {"fingerprint": fingerprint, "workloads": {}}
+    rec["workloads"][workload] = res
+    rec["calibration"] = {"copy_mib": copy_mib, "fetch_kib_read": f_cal, "write_kib_read": w_cal,
+                          "fetch_scale": f_scale, "write_scale": w_scale}
+    json.dump(rec, open(out_json, "w"), indent=1)
+    md = [f"# HBM traffic per launch, {workload}", "",
+          f"Commands: `{command}` (one run with `--pmc FETCH_SIZE`, one with `--pmc WRITE_SIZE`).", "",
+          f"Calibration: dst = src * 1 over {copy_mib} MiB float32; FETCH_SIZE read {f_cal:.0f} and "
+          f"WRITE_SIZE {w_cal:.0f} for {known / 1024:.0f} KiB moved each way, so the counters are "
+          f"scaled by {f_scale:.4f} (fetch) and {w_scale:.4f} (write) bytes per unit.", "",
+          f"Kernel source fingerprint: `{fingerprint}`", "",
+          "| kernel | fetch MB | write MB | total MB |", "|---|---|---|---|", *lines]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--out-json", required=True)
+    t.add_argument("--out-md", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--fingerprint", required=True)
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        stats(a.csv, a.out, a.command)
+    else:
+        traffic(a.fetch_csv, a.write_csv, a.workload, a.copy_mib, a.out_json, a.out_md, a.command,
+                a.fingerprint)
+
+
+if __name__ == "__main__":
+    main()
