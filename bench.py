@@ -40,8 +40,8 @@ def flops(wl) -> dict:
     return {
         "fwd": n2 * (wl.dk + wl.dv),                 # S = QK^T, O = PV
         "bwd": n2 * (3 * wl.dk + 2 * wl.dv),         # S recompute, dP, dV, dK, dQ
-        "bwd_dkdv": n2 * (2 * wl.dk + 2 * wl.dv),    # kernel: S, dP, dV, dK
-        "bwd_dq": n2 * (2 * wl.dk + wl.dv),          # kernel: S, dP, dQ (S, dP recomputed)
+        "bwd_dkdv": n2 * (2 * wl.dk + 2 * wl.dv),    # dK/dV pass: S, dP, dV, dK
+        "bwd_dq": n2 * (2 * wl.dk + wl.dv),          # dQ pass: S, dP, dQ (S, dP recomputed)
     }
 
 
@@ -157,11 +157,56 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
     }
 
 
+def time_workload_graph(torch, wl, steps: int, warmup: int) -> dict:
+    """The same fwd+bwd step captured once into a HIP graph and replayed:
+    per-call GPU time without host launch overhead (what a caller that
+    captures its step sees).  Library timing is off during capture."""
+    from vision_transformer_attention_psa_amd import binding, inputs
+    x = inputs.make_inputs(wl)
+    qkv, dO = device_inputs(torch, x)
+    o = torch.empty((wl.B, wl.heads, wl.dv, wl.N), dtype=qkv.dtype, device="cuda")
+    lse = torch.empty((wl.B, wl.heads, wl.N), dtype=torch.float32, device="cuda")
+    d = torch.empty_like(qkv)
+    binding.psa_attn_timing_enable(False)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the scratch cache for the capture stream
+        binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+        binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gf, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf, stream=s):
+        binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+    with torch.cuda.graph(gb, stream=s):
+        binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+    for _ in range(warmup):
+        gf.replay()
+        gb.replay()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for _ in range(steps):
+        gf.replay()
+    e[1].record()
+    for _ in range(steps):
+        gb.replay()
+    e[2].record()
+    torch.cuda.synchronize()
+    fl = flops(wl)
+    fwd_us = e[0].elapsed_time(e[1]) * 1e3 / steps
+    bwd_us = e[1].elapsed_time(e[2]) * 1e3 / steps
+    return {"fwd_us": fwd_us, "bwd_us": bwd_us, "bwd_tflops": fl["bwd"] / (bwd_us * 1e-6) / 1e12}
+
+
 def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
-    per_launch = {"fwd": fl["fwd"], "bwd_dkdv": fl["bwd_dkdv"], "bwd_dq": fl["bwd_dq"]}
     us = r["kernel_avg_us"]
+    if us.get("bwd_dq") == us.get("bwd_dq"):  # split build: dK/dV and dQ launched separately
+        per_launch = {"fwd": fl["fwd"], "bwd_main": fl["bwd_dkdv"], "bwd_dq": fl["bwd_dq"]}
+    else:  # one backward launch computes dQ, dK and dV
+        per_launch = {"fwd": fl["fwd"], "bwd_main": fl["bwd"]}
     name = max(per_launch, key=lambda k: us[k])
     achieved = per_launch[name] / (us[name] * 1e-6) / 1e12
     return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": r["peak_tflops"],
@@ -212,6 +257,7 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--also", default=",".join(ALSO), help="comma list of extra workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--graph", type=int, default=1, help="also time HIP-graph replay of the step (1/0)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain MIB-MiB device copy first (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -243,6 +289,12 @@ def main() -> int:
                                         "fwd_bwd_tflops", "fwd_bwd_pct_mfma_peak", "kernel_avg_us")}
         print(f"[bench] {name}: fwd {a['fwd_us']:.1f} us, bwd {a['bwd_us']:.1f} us, "
               f"bwd {a['bwd_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    graph = {}
+    if args.graph:
+        for name in [wl.name] + [a for a in args.also.split(",") if a]:
+            graph[name] = time_workload_graph(torch, inputs.WORKLOADS[name], args.steps, args.warmup)
+            print(f"[bench] graph replay {name}: fwd {graph[name]['fwd_us']:.1f} us, "
+                  f"bwd {graph[name]['bwd_us']:.1f} us", file=sys.stderr, flush=True)
     traffic = load_traffic(wl.name)
     cpu = None
     if args.cpu_budget > 0:
@@ -273,6 +325,7 @@ def main() -> int:
         "roofline": roofline(wl, r, traffic),
         "cpu_baseline": cpu,
         "also": also,
+        "graph_replay": graph,
     }
     print(json.dumps(out), flush=True)
     return 0

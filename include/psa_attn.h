@@ -79,8 +79,9 @@ int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N,
  *                  section 1 = dK, section 2 = dV, each element written
  *                  exactly once (deterministic: bitwise identical results
  *                  run to run; no floating-point atomics)
- * Scratch: 8*B*heads*N bytes of device memory, taken stream-ordered from
- * `stream` (hipMallocAsync) and released stream-ordered before returning.
+ * Scratch: 8*B*heads*N bytes of device memory from a grow-only buffer the
+ * library keeps per (device, stream) until the process ends; the first call
+ * on a stream (or a larger one) allocates it with hipMalloc.
  */
 int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dO,
                  void* d_packed, int B, int heads, int N, int dk, int dv, float scale,
@@ -102,7 +103,8 @@ int psa_attn_version(void);
  * bracketed by two hipEvents recorded on the launch stream; durations are
  * accumulated per kernel.  Off by default; process-wide, thread-safe.
  * Kernel slots: 0 = forward, 1 = backward preprocess (D, LSE*log2 e),
- * 2 = backward dK/dV, 3 = backward dQ.
+ * 2 = backward GEMM launch (dK/dV and dQ in one grid), 3 = backward dQ
+ * (used only by builds with -DPSA_BWD_SPLIT=1, where slot 2 is dK/dV).
  */
 #define PSA_TIMING_SLOTS 4
 /* on != 0 enables, 0 disables.  Returns PSA_OK. */

@@ -21,7 +21,7 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPP
 EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_supported", "psa_last_error",
            "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
            "psa_attn_timing_reset")
-TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq")
 
 _lib = None
 

@@ -9,8 +9,10 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "psa_kernels.h"
@@ -24,10 +26,11 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
-// Tile shapes per element type.  bf16 fragments take half the registers of
-// fp32 ones, so bf16 tiles are twice as wide in the stationary dimension.
-template <typename T> struct Tiles;
-// Defaults can be overridden at build time (-DPSA_BF16_FWD_QB=...) for tuning.
+// Tile shapes.  Wide tiles (64 queries per wave in the forward, 32 keys or
+// queries per wave in the backward) reuse each LDS fragment over more MFMAs;
+// small sequences use 16 per wave so that the grid still fills 256 CUs.
+// bf16 fragments take half the registers of fp32 ones.  Defaults can be
+// overridden at build time (-DPSA_BF16_FWD_QB=...) for tuning.
 #ifndef PSA_BF16_FWD_QB
 #define PSA_BF16_FWD_QB 4
 #endif
@@ -37,31 +40,40 @@ template <typename T> struct Tiles;
 #ifndef PSA_BF16_DKDV_KB
 #define PSA_BF16_DKDV_KB 2
 #endif
-#ifndef PSA_BF16_DKDV_NW
-#define PSA_BF16_DKDV_NW 4
-#endif
 #ifndef PSA_BF16_DKDV_BMQ
 #define PSA_BF16_DKDV_BMQ 64
 #endif
 #ifndef PSA_BF16_DQ_QB
 #define PSA_BF16_DQ_QB 2
 #endif
-#ifndef PSA_BF16_DQ_NW
-#define PSA_BF16_DQ_NW 4
+#ifndef PSA_BWD_SPLIT
+#define PSA_BWD_SPLIT 0  // 1: separate dK/dV and dQ launches (per-pass timing)
 #endif
-template <> struct Tiles<psa::bf16> {
+#ifndef PSA_SMALL_N_MAX
+#define PSA_SMALL_N_MAX 512  // sequences up to this length use the narrow tiles
+#endif
+template <typename T> struct TilesWide;
+template <> struct TilesWide<psa::bf16> {
   static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = PSA_BF16_FWD_QB, FWD_BN = 64;
-  static constexpr int DKDV_NW = PSA_BF16_DKDV_NW, DKDV_KB = PSA_BF16_DKDV_KB, DKDV_BMQ = PSA_BF16_DKDV_BMQ;
-  static constexpr int DQ_NW = PSA_BF16_DQ_NW, DQ_QB = PSA_BF16_DQ_QB, DQ_BN = 64;
+  static constexpr int DKDV_KB = PSA_BF16_DKDV_KB, DKDV_BMQ = PSA_BF16_DKDV_BMQ;
+  static constexpr int DQ_QB = PSA_BF16_DQ_QB, DQ_BN = 64;
 };
-template <> struct Tiles<float> {
+template <> struct TilesWide<float> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
-  static constexpr int DKDV_NW = 4, DKDV_KB = 1, DKDV_BMQ = 32;
-  static constexpr int DQ_NW = 4, DQ_QB = 1, DQ_BN = 32;
+  static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
+  static constexpr int DQ_QB = 1, DQ_BN = 32;
 };
+template <typename T> struct TilesNarrow {
+  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
+  static constexpr int DKDV_KB = 1, DKDV_BMQ = 64;
+  static constexpr int DQ_QB = 1, DQ_BN = 64;
+};
+template <> struct TilesNarrow<float> : TilesWide<float> {};
 
 // ------------------------------------------------------- per-kernel timing
-enum { K_FWD = 0, K_PRE = 1, K_DKDV = 2, K_DQ = 3 };
+// Slots: forward; D/LSE preprocessing; the backward GEMM launch (fused dK/dV
+// + dQ, or dK/dV alone when split); dQ when split.
+enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3 };
 
 struct Timing {
   std::mutex mu;
@@ -113,6 +125,43 @@ struct TimedLaunch {
   }
 };
 
+// ------------------------------------------------------------ scratch cache
+// One grow-only device buffer per (device, stream).  A buffer is only ever
+// reused by later calls on the same stream, which stream order serialises;
+// growing waits for the stream before releasing the old buffer.  Buffers
+// live until the process ends.
+struct ScratchCache {
+  std::mutex mu;
+  std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> bufs;
+};
+ScratchCache g_scratch;
+
+void* scratch_for(hipStream_t st, size_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    g_err = "psa_attn_bwd: no HIP device";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  auto& slot = g_scratch.bufs[{dev, st}];
+  if (slot.second >= bytes) return slot.first;
+  if (slot.first) {
+    if (hipStreamSynchronize(st) != hipSuccess || hipFree(slot.first) != hipSuccess) {
+      g_err = "psa_attn_bwd: releasing the old scratch buffer failed";
+      return nullptr;
+    }
+    slot = {nullptr, 0};
+  }
+  const size_t want = bytes + bytes / 4;  // headroom against repeated growth
+  void* p = nullptr;
+  if (hipMalloc(&p, want) != hipSuccess || p == nullptr) {
+    g_err = "psa_attn_bwd: scratch allocation of " + std::to_string(want) + " bytes failed";
+    return nullptr;
+  }
+  slot = {p, want};
+  return p;
+}
+
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -121,9 +170,8 @@ int check_launch(const char* what) {
 
 template <typename T> constexpr bool vec_ok(int N) { return N % (16 / (int)sizeof(T)) == 0; }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, class C>
 int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hipStream_t st) {
-  using C = Tiles<T>;
   constexpr int BM = C::FWD_NW * 16 * C::FWD_QB;
   const int nqt = (N + BM - 1) / BM;
   const long long grid = (long long)BH * nqt;
@@ -140,22 +188,19 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hi
   return check_launch("psa_attn_fwd launch");
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, class C>
 int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, void* dpk, int BH, int N,
             float scale, hipStream_t st) {
-  using C = Tiles<T>;
   const float c = scale * psa::kLog2e;
   const long long total = (long long)BH * N;
-  constexpr int BNK = C::DKDV_NW * 16 * C::DKDV_KB;
-  constexpr int BMD = C::DQ_NW * 16 * C::DQ_QB;
+  constexpr int BNK = 4 * 16 * C::DKDV_KB;  // keys per dK/dV workgroup
+  constexpr int BMD = 4 * 16 * C::DQ_QB;    // queries per dQ workgroup
   const int nkt = (N + BNK - 1) / BNK, nqt = (N + BMD - 1) / BMD;
-  if ((long long)BH * nkt > INT32_MAX || (long long)BH * nqt > INT32_MAX)
-    return fail(PSA_ERR_SHAPE, "psa_attn_bwd: grid too large");
+  if ((long long)BH * (nkt + nqt) > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_attn_bwd: grid too large");
+  const int nkb = BH * nkt, nqb = BH * nqt;
 
-  float2* stats = nullptr;
-  hipError_t e = hipMallocAsync((void**)&stats, (size_t)total * sizeof(float2), st);
-  if (e != hipSuccess || stats == nullptr)
-    return fail(PSA_ERR_NOMEM, std::string("psa_attn_bwd: scratch allocation failed: ") + hipGetErrorString(e));
+  float2* stats = (float2*)scratch_for(st, (size_t)total * sizeof(float2));
+  if (stats == nullptr) return PSA_ERR_NOMEM;
 
   int rc;
   {
@@ -164,31 +209,43 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
                        (const T*)o, (const T*)dO, lse, stats, N, (int)total);
     rc = check_launch("psa_attn_bwd preprocess launch");
   }
-  if (rc == PSA_OK) {
-    const dim3 gk((unsigned)(BH * nkt)), bk(C::DKDV_NW * 64);
-    TimedLaunch tl(K_DKDV, st);
+  if (rc != PSA_OK) return rc;
+#if PSA_BWD_SPLIT
+  {
+    TimedLaunch tl(K_MAIN, st);
     if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_NW, C::DKDV_BMQ, true>), gk, bk, 0,
-                         st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
-    else
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_NW, C::DKDV_BMQ, false>), gk, bk,
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, true>), dim3(nkb), dim3(256),
                          0, st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
+    else
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, false>), dim3(nkb),
+                         dim3(256), 0, st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
     rc = check_launch("psa_attn_bwd dK/dV launch");
   }
   if (rc == PSA_OK) {
-    const dim3 gq((unsigned)(BH * nqt)), bq(C::DQ_NW * 64);
     TimedLaunch tl(K_DQ, st);
     if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, C::DQ_NW, C::DQ_BN, true>), gq, bq, 0, st,
+      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, true>), dim3(nqb), dim3(256), 0, st,
                          (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
     else
-      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, C::DQ_NW, C::DQ_BN, false>), gq, bq, 0, st,
-                         (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
+      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, false>), dim3(nqb), dim3(256), 0,
+                         st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
     rc = check_launch("psa_attn_bwd dQ launch");
   }
-  e = hipFreeAsync(stats, st);
-  if (rc == PSA_OK && e != hipSuccess)
-    rc = fail(PSA_ERR_HIP, std::string("psa_attn_bwd: scratch release failed: ") + hipGetErrorString(e));
+#else
+  {
+    TimedLaunch tl(K_MAIN, st);
+    const dim3 grid((unsigned)(nkb + nqb)), block(256);
+    if (vec_ok<T>(N))
+      hipLaunchKernelGGL(
+          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, true>), grid, block, 0,
+          st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, nqt, nkb, c, scale);
+    else
+      hipLaunchKernelGGL(
+          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, false>), grid, block, 0,
+          st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, nqt, nkb, c, scale);
+    rc = check_launch("psa_attn_bwd launch");
+  }
+#endif
   return rc;
 }
 
@@ -326,8 +383,10 @@ int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N, 
     return fail(PSA_ERR_ALIAS, "psa_attn_fwd: o, lse and qkv must not overlap");
   if ((rc = check_device(fn)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-#define X(DT, T, K, V) \
-  if (dtype == DT && dk == K && dv == V) return run_fwd<T, K, V>(qkv, o, lse, (int)BH, N, scale, st);
+#define X(DT, T, K, V)                                                                     \
+  if (dtype == DT && dk == K && dv == V)                                                   \
+    return N <= PSA_SMALL_N_MAX ? run_fwd<T, K, V, TilesNarrow<T>>(qkv, o, lse, (int)BH, N, scale, st) \
+                                : run_fwd<T, K, V, TilesWide<T>>(qkv, o, lse, (int)BH, N, scale, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, "psa_attn_fwd: no instance");
@@ -353,8 +412,11 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
     return fail(PSA_ERR_ALIAS, "psa_attn_bwd: d_packed must not overlap any input");
   if ((rc = check_device(fn)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-#define X(DT, T, K, V) \
-  if (dtype == DT && dk == K && dv == V) return run_bwd<T, K, V>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st);
+#define X(DT, T, K, V)                                                                              \
+  if (dtype == DT && dk == K && dv == V)                                                            \
+    return N <= PSA_SMALL_N_MAX                                                                     \
+               ? run_bwd<T, K, V, TilesNarrow<T>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st) \
+               : run_bwd<T, K, V, TilesWide<T>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, "psa_attn_bwd: no instance");

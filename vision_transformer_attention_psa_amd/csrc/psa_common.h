@@ -288,6 +288,15 @@ struct Stager<float, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
   }
 };
 
+// Workgroup barrier that orders LDS accesses only: global loads still in
+// flight (prefetches into registers) are not waited for, unlike
+// __syncthreads(), whose fence also covers global memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Remap so
 // that consecutive logical ids (tiles of one (batch, head) slice, which share
 // K/V or Q/dO) run on the same XCD and share its L2.  Bijective for any n.

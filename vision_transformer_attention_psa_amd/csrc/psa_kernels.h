@@ -36,6 +36,14 @@ namespace psa {
 
 constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before a rescale
 
+// Optional occupancy hint for the compute kernels (waves per SIMD the
+// register allocator may plan for); empty unless set at build time.
+#ifdef PSA_WAVES_PER_EU
+#define PSA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PSA_WAVES_PER_EU, PSA_WAVES_PER_EU)))
+#else
+#define PSA_OCCUPANCY
+#endif
+
 template <int D> struct Chunks {
   static constexpr int n = (D + 31) / 32;  // 32-wide contraction chunks
   static_assert(D % 16 == 0, "head dims must be multiples of 16");
@@ -46,7 +54,7 @@ __device__ __forceinline__ T* tm_of(T* base, const S&) { return base + S::NAT_EL
 
 // =================================================================== forward
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
-__global__ __launch_bounds__(NW * 64) void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
+__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
                                                          float* __restrict__ lse, int N, int n_qtiles,
                                                          float c /* scale * log2(e) */) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
@@ -214,26 +222,36 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
 }
 
 // ============================================================ backward dK/dV
+// Key-stationary body: workgroup `blk` owns BNK = NW*16*KB keys of one slice
+// and streams the queries in tiles of BMQ through a double-buffered LDS tile.
+template <typename T, int DK, int DV, int KB, int NW, int BMQ>
+struct DkdvShape {
+  static constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
+  // Q|dO tile: both layouts of every row.  K|V stationary tile: token-major.
+  using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, DK + DV, 0, DK + DV>;
+  using SKV = Stager<T, DK + DV, BNK, NT, true, DK + DV, DK + DV, 0, 0>;
+  static constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 2 * BMQ * (int)sizeof(float2);
+  static constexpr int KV_BYTES = (SKV::NAT_ELEMS + SKV::TM_ELEMS) * (int)sizeof(T);
+  static constexpr int SMEM = QG_BYTES > KV_BYTES ? QG_BYTES : KV_BYTES;
+};
+
 template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
-__global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
-    T* __restrict__ dpk, int N, int n_ktiles, float c, float scale) {
-  constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
+__device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T* __restrict__ dO,
+                                              const float2* __restrict__ stats, T* __restrict__ dpk, int N,
+                                              int n_ktiles, float c, float scale, int blk,
+                                              unsigned char* smem_raw) {
+  using Shape = DkdvShape<T, DK, DV, KB, NW, BMQ>;
+  constexpr int KW = Shape::KW, BNK = Shape::BNK, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BMQ % 32 == 0, "query tile must be a multiple of 32");
-  // Q|dO tile: both layouts of every row.  K|V stationary tile: token-major.
   using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, DK + DV, 0, DK + DV>;
   using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK + DV, DK + DV, 0, 0>;
   constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
-  constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 2 * BMQ * (int)sizeof(float2);
-  constexpr int KV_BYTES = (SKV::NAT_ELEMS + SKV::TM_ELEMS) * (int)sizeof(T);
-  constexpr int SMEM = QG_BYTES > KV_BYTES ? QG_BYTES : KV_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM];
   T* smem = (T*)smem_raw;
   float2* sstats = (float2*)(smem_raw + 2 * TILE * sizeof(T));
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / n_ktiles, j0 = (blk - bh * n_ktiles) * BNK;
   const size_t C = 2 * DK + DV;
   const T* Qg = qkv + (size_t)bh * C * N;
@@ -286,13 +304,24 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
 
 #pragma unroll
     for (int c2 = 0; c2 < BMQ / 32; ++c2) {
+      // Rows of block h are the queries 32*c2 + 8g + 4h + r (r = register).
+      float nl[2][4], nd[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float2 q = sq[32 * c2 + 8 * g + 4 * h + r];
+          nl[h][r] = -q.x;
+          nd[h][r] = -q.y;
+        }
       f32x4 s[2][KB], dp[2][KB];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        // dP accumulates on top of -D, so that dS = P * acc.
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h][kb] = f32x4{nd[h][0], nd[h][1], nd[h][2], nd[h][3]};
         }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -308,15 +337,13 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(dp[h][kb], a, vf[kb][cc]);
         }
-        // rows of block h: queries 32*c2 + 8g + 4h + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float2 q = sq[32 * c2 + 8 * g + 4 * h + r];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            const float p = fast_exp2(__builtin_fmaf(s[h][kb][r], c, -q.x));
+            const float p = fast_exp2(__builtin_fmaf(s[h][kb][r], c, nl[h][r]));
             s[h][kb][r] = p;
-            dp[h][kb][r] = p * (dp[h][kb][r] - q.y);
+            dp[h][kb][r] *= p;
           }
         }
       }
@@ -371,33 +398,44 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dkdv_kernel(
 }
 
 // =============================================================== backward dQ
+// Query-stationary body: workgroup `blk` owns BM = NW*16*QB queries of one
+// slice and streams the keys in tiles of BN through a double-buffered tile.
+template <typename T, int DK, int DV, int QB, int NW, int BN>
+struct DqShape {
+  static constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
+  // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T).
+  using SKV = Stager<T, DK + DV, BN, NT, true, DK + DV, DK + DV, 0, DK>;
+  // Stationary Q|dO tile, token-major.
+  using SQG = Stager<T, DK + DV, BM, NT, true, DK, DK + DV, 0, 0>;
+  static constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
+  static constexpr int QE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  static constexpr int SMEM = (2 * BUF > QE ? 2 * BUF : QE) * (int)sizeof(T);
+};
+
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
-__global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
-    T* __restrict__ dpk, int N, int n_qtiles, float c, float scale) {
-  constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
+__device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* __restrict__ dO,
+                                            const float2* __restrict__ stats, T* __restrict__ dpk, int N,
+                                            int n_qtiles, float c, float scale, int blk, unsigned char* smem_raw) {
+  using Shape = DqShape<T, DK, DV, QB, NW, BN>;
+  constexpr int QW = Shape::QW, BM = Shape::BM, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
-  // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T).
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK + DV, DK + DV, 0, DK>;
-  // Stationary Q|dO tile, token-major.
   using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, DK + DV, 0, 0>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
-  constexpr int QE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
-  constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
-  __shared__ __attribute__((aligned(16))) T smem[SMEM];
+  T* smem = (T*)smem_raw;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
   const size_t C = 2 * DK + DV;
   const T* Qg = qkv + (size_t)bh * C * N;
   const T* KVg = Qg + (size_t)DK * N;
   const T* dOg = dO + (size_t)bh * DV * N;
 
-  // Stationary queries: B operands of S^T = K Q^T and dP^T = V dO^T.
+  // Stationary queries: B operands of S^T = K Q^T and dP^T = V dO^T.  Their
+  // LSE (log2 units, negated) and -D are per lane (lane column = query).
   Frag<T> qf[QB][KC], gf[QB][CC];
-  float lse2[QB], dd[QB];
+  float nl[QB], nd[QB];
   {
     SQG sq;
     sq.load(Qg, dOg, N, i0, tid);
@@ -414,8 +452,8 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
         frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
       const int i = i0 + row0 + t;
       const float2 q = (i < N) ? stats[(size_t)bh * N + i] : make_float2(kPosInf, 0.f);
-      lse2[nb] = q.x;
-      dd[nb] = q.y;
+      nl[nb] = -q.x;
+      nd[nb] = -q.y;
     }
     __syncthreads();
   }
@@ -444,10 +482,11 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
       f32x4 s[2][QB], dp[2][QB];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        // dP^T accumulates on top of -D, so that dS^T = P^T * acc.
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) {
           s[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h][nb] = f32x4{nd[nb], nd[nb], nd[nb], nd[nb]};
         }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -468,8 +507,8 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
           const bool dead = tail && (j0 + 32 * c2 + 8 * g + 4 * h + r >= N);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) {
-            const float p = dead ? 0.f : fast_exp2(__builtin_fmaf(s[h][nb][r], c, -lse2[nb]));
-            dp[h][nb][r] = p * (dp[h][nb][r] - dd[nb]);
+            const float p = dead ? 0.f : fast_exp2(__builtin_fmaf(s[h][nb][r], c, nl[nb]));
+            dp[h][nb][r] *= p;
           }
         }
       }
@@ -504,6 +543,45 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_dq_kernel(
           dpk[((size_t)bh * C + 16 * db + 4 * g + r) * N + i] = from_f32<T>(dqacc[db][nb][r] * scale);
     }
   }
+}
+
+// ========================================================= backward kernels
+template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
+__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dkdv_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
+    T* __restrict__ dpk, int N, int n_ktiles, float c, float scale) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM];
+  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, stats, dpk, N, n_ktiles, c, scale,
+                                               xcd_remap(blockIdx.x, gridDim.x), smem);
+}
+
+template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
+__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
+    T* __restrict__ dpk, int N, int n_qtiles, float c, float scale) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[DqShape<T, DK, DV, QB, NW, BN>::SMEM];
+  bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, stats, dpk, N, n_qtiles, c, scale,
+                                             xcd_remap(blockIdx.x, gridDim.x), smem);
+}
+
+// Both backward GEMM chains in one launch: the first n_kblocks workgroups
+// are key-stationary (dK, dV), the rest query-stationary (dQ).  The long
+// dK/dV workgroups are dispatched first and the shorter dQ ones fill the
+// machine behind them, so neither pass leaves a partly idle last wave of
+// workgroups on its own; both share one LDS allocation.
+template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, bool VECOK>
+__global__ __launch_bounds__(256) PSA_OCCUPANCY void psa_bwd_fused_kernel(
+    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
+    T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, float c, float scale) {
+  constexpr int S1 = DkdvShape<T, DK, DV, KB, 4, BMQ>::SMEM, S2 = DqShape<T, DK, DV, QB, 4, BN>::SMEM;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S1 > S2 ? S1 : S2];
+  const int b = blockIdx.x;
+  if (b < n_kblocks)
+    bwd_dkdv_body<T, DK, DV, KB, 4, BMQ, VECOK>(qkv, dO, stats, dpk, N, n_ktiles, c, scale,
+                                                xcd_remap(b, n_kblocks), smem);
+  else
+    bwd_dq_body<T, DK, DV, QB, 4, BN, VECOK>(qkv, dO, stats, dpk, N, n_qtiles, c, scale,
+                                             xcd_remap(b - n_kblocks, (int)gridDim.x - n_kblocks), smem);
 }
 
 }  // namespace psa

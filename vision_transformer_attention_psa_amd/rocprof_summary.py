@@ -21,7 +21,8 @@ import sys
 from collections import defaultdict
 
 PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
-             ("psa_bwd_dkdv_kernel", "bwd_dkdv"), ("psa_bwd_dq_kernel", "bwd_dq"))
+             ("psa_bwd_fused_kernel", "bwd_main"), ("psa_bwd_dkdv_kernel", "bwd_main"),
+             ("psa_bwd_dq_kernel", "bwd_dq"))
 
 
 def short_name(kernel: str) -> str:
