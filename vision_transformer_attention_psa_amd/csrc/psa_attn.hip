@@ -181,10 +181,10 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hi
   TimedLaunch tl(K_FWD, st);
   if (vec_ok<T>(N))
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true>), g, b, 0, st,
-                       (const T*)qkv, (T*)o, lse, N, nqt, c);
+                       (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c);
   else
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, false>), g, b, 0, st,
-                       (const T*)qkv, (T*)o, lse, N, nqt, c);
+                       (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c);
   return check_launch("psa_attn_fwd launch");
 }
 
@@ -199,8 +199,10 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   if ((long long)BH * (nkt + nqt) > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_attn_bwd: grid too large");
   const int nkb = BH * nkt, nqb = BH * nqt;
 
-  float2* stats = (float2*)scratch_for(st, (size_t)total * sizeof(float2));
+  float* stats = (float*)scratch_for(st, (size_t)total * 2 * sizeof(float));  // planes -LSE log2 e, -D
   if (stats == nullptr) return PSA_ERR_NOMEM;
+  const float* nl = stats;
+  const float* nd = stats + total;
 
   int rc;
   {
@@ -215,20 +217,20 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     TimedLaunch tl(K_MAIN, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, true>), dim3(nkb), dim3(256),
-                         0, st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
+                         0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale);
     else
       hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, false>), dim3(nkb),
-                         dim3(256), 0, st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, c, scale);
+                         dim3(256), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale);
     rc = check_launch("psa_attn_bwd dK/dV launch");
   }
   if (rc == PSA_OK) {
     TimedLaunch tl(K_DQ, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, true>), dim3(nqb), dim3(256), 0, st,
-                         (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
+                         (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale);
     else
       hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, false>), dim3(nqb), dim3(256), 0,
-                         st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nqt, c, scale);
+                         st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale);
     rc = check_launch("psa_attn_bwd dQ launch");
   }
 #else
@@ -238,11 +240,11 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     if (vec_ok<T>(N))
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, true>), grid, block, 0,
-          st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, nqt, nkb, c, scale);
+          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale);
     else
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, false>), grid, block, 0,
-          st, (const T*)qkv, (const T*)dO, stats, (T*)dpk, N, nkt, nqt, nkb, c, scale);
+          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale);
     rc = check_launch("psa_attn_bwd launch");
   }
 #endif

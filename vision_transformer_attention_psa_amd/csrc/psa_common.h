@@ -72,7 +72,14 @@ template <> __device__ __forceinline__ Frag<float> ones_frag<float>() {
   return f;
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Work-item / workgroup ids straight from the hardware registers (the
+// threadIdx / blockIdx accessors go through device-library calls that are
+// not inlined into code built without packed-fp32 instructions).  Kernels
+// take their grid size as an argument rather than reading the dispatch
+// packet, which may live in host memory.
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int block_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int lane_id() { return thread_id() & 63; }
 
 // Token of row m (0..15) of score block h within a 32-token chunk.
 __device__ __forceinline__ int perm_row(int m, int h) { return 8 * (m >> 2) + 4 * h + (m & 3); }

@@ -56,7 +56,7 @@ __device__ __forceinline__ T* tm_of(T* base, const S&) { return base + S::NAT_EL
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
                                                          float* __restrict__ lse, int N, int n_qtiles,
-                                                         float c /* scale * log2(e) */) {
+                                                         int n_blocks, float c /* scale * log2(e) */) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
@@ -69,8 +69,8 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
   constexpr int VROW = is_bf16<T>() ? 0 : DK;  // first V row in the channel-major tile
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int blk = xcd_remap(block_id(), n_blocks);
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
   const T* Qg = qkv + (size_t)bh * (2 * DK + DV) * N;
   const T* KVg = Qg + (size_t)DK * N;
@@ -205,12 +205,16 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
 }
 
 // ========================================================= backward: D, LSE2
-// stats[q] = {LSE_q * log2(e), D_q} for every query of every slice.
+// nl[q] = -LSE_q * log2(e) and nd[q] = -D_q for every query of every slice
+// (two planes of `total` floats): both are only ever subtracted (exp2(S c -
+// LSE log2 e) and dP - D), and stored negated they enter an FMA or an MFMA
+// accumulator input as they are; four consecutive queries are one 16-byte
+// LDS read.
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO,
-                                                          const float* __restrict__ lse,
-                                                          float2* __restrict__ stats, int N, int total) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+                                                          const float* __restrict__ lse, float* __restrict__ stats,
+                                                          int N, int total) {
+  const int idx = block_id() * 256 + thread_id();
   if (idx >= total) return;
   const int bh = idx / N, i = idx - bh * N;
   const T* op = o + (size_t)bh * DV * N + i;
@@ -218,7 +222,8 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
   float d = 0.f;
 #pragma unroll 16
   for (int ch = 0; ch < DV; ++ch) d = __builtin_fmaf(to_f32(op[(size_t)ch * N]), to_f32(gp[(size_t)ch * N]), d);
-  stats[idx] = make_float2(lse[idx] * kLog2e, d);
+  stats[idx] = -lse[idx] * kLog2e;
+  stats[(size_t)total + idx] = -d;
 }
 
 // ============================================================ backward dK/dV
@@ -231,14 +236,16 @@ struct DkdvShape {
   using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, DK + DV, 0, DK + DV>;
   using SKV = Stager<T, DK + DV, BNK, NT, true, DK + DV, DK + DV, 0, 0>;
   static constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
-  static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 2 * BMQ * (int)sizeof(float2);
+  static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 4 * BMQ * (int)sizeof(float);
+  static_assert(2 * TILE * sizeof(T) % 16 == 0, "statistics must be 16-byte aligned");
   static constexpr int KV_BYTES = (SKV::NAT_ELEMS + SKV::TM_ELEMS) * (int)sizeof(T);
   static constexpr int SMEM = QG_BYTES > KV_BYTES ? QG_BYTES : KV_BYTES;
 };
 
 template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
 __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T* __restrict__ dO,
-                                              const float2* __restrict__ stats, T* __restrict__ dpk, int N,
+                                              const float* __restrict__ nlg, const float* __restrict__ ndg,
+                                              T* __restrict__ dpk, int N,
                                               int n_ktiles, float c, float scale, int blk,
                                               unsigned char* smem_raw) {
   using Shape = DkdvShape<T, DK, DV, KB, NW, BMQ>;
@@ -249,15 +256,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK + DV, DK + DV, 0, 0>;
   constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   T* smem = (T*)smem_raw;
-  float2* sstats = (float2*)(smem_raw + 2 * TILE * sizeof(T));
+  float* snl = (float*)(smem_raw + 2 * TILE * sizeof(T));  // [2][BMQ], then snd [2][BMQ]
+  float* snd = snl + 2 * BMQ;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int bh = blk / n_ktiles, j0 = (blk - bh * n_ktiles) * BNK;
   const size_t C = 2 * DK + DV;
   const T* Qg = qkv + (size_t)bh * C * N;
   const T* KVg = Qg + (size_t)DK * N;
   const T* dOg = dO + (size_t)bh * DV * N;
-  const float2* st = stats + (size_t)bh * N;
+  const float* nlq = nlg + (size_t)bh * N;
+  const float* ndq = ndg + (size_t)bh * N;
 
   // Stationary keys: B operands of S = Q K^T and dP = dO V^T (lane = key).
   Frag<T> kf[KB][KC], vf[KB][CC];
@@ -291,7 +300,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   SQG sg;
   sg.load(Qg, dOg, N, 0, tid);
   sg.store(smem, tm_of(smem, sg), tid);
-  for (int q = tid; q < BMQ; q += NT) sstats[q] = q < N ? st[q] : make_float2(kPosInf, 0.f);
+  for (int q = tid; q < BMQ; q += NT) {  // padding rows: P = 0
+    snl[q] = q < N ? nlq[q] : kNegInf;
+    snd[q] = q < N ? ndq[q] : 0.f;
+  }
   __syncthreads();
 
   const int nqt = (N + BMQ - 1) / BMQ;
@@ -299,21 +311,19 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
     const int cur = qt & 1;
     const T* nat = smem + cur * TILE;   // rows: Q channels, then dO channels
     const T* tm = tm_of(nat, sg);       // columns: Q channels, then dO channels
-    const float2* sq = sstats + cur * BMQ;
+    const float* sl = snl + cur * BMQ;
+    const float* sd = snd + cur * BMQ;
     if (qt + 1 < nqt) sg.load(Qg, dOg, N, (qt + 1) * BMQ, tid);
 
 #pragma unroll
     for (int c2 = 0; c2 < BMQ / 32; ++c2) {
       // Rows of block h are the queries 32*c2 + 8g + 4h + r (r = register).
-      float nl[2][4], nd[2][4];
+      f32x4 nl[2], nd[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float2 q = sq[32 * c2 + 8 * g + 4 * h + r];
-          nl[h][r] = -q.x;
-          nd[h][r] = -q.y;
-        }
+      for (int h = 0; h < 2; ++h) {
+        nl[h] = *(const f32x4*)(sl + 32 * c2 + 8 * g + 4 * h);
+        nd[h] = *(const f32x4*)(sd + 32 * c2 + 8 * g + 4 * h);
+      }
       f32x4 s[2][KB], dp[2][KB];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -321,7 +331,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[h][kb] = f32x4{nd[h][0], nd[h][1], nd[h][2], nd[h][3]};
+          dp[h][kb] = nd[h];
         }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -374,8 +384,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
       T* nx = smem + (cur ^ 1) * TILE;
       sg.store(nx, tm_of(nx, sg), tid);
       const int q0 = (qt + 1) * BMQ;
-      for (int q = tid; q < BMQ; q += NT)
-        sstats[(cur ^ 1) * BMQ + q] = q0 + q < N ? st[q0 + q] : make_float2(kPosInf, 0.f);
+      for (int q = tid; q < BMQ; q += NT) {
+        snl[(cur ^ 1) * BMQ + q] = q0 + q < N ? nlq[q0 + q] : kNegInf;
+        snd[(cur ^ 1) * BMQ + q] = q0 + q < N ? ndq[q0 + q] : 0.f;
+      }
     }
     __syncthreads();
   }
@@ -414,7 +426,8 @@ struct DqShape {
 
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
 __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* __restrict__ dO,
-                                            const float2* __restrict__ stats, T* __restrict__ dpk, int N,
+                                            const float* __restrict__ nlg, const float* __restrict__ ndg,
+                                            T* __restrict__ dpk, int N,
                                             int n_qtiles, float c, float scale, int blk, unsigned char* smem_raw) {
   using Shape = DqShape<T, DK, DV, QB, NW, BN>;
   constexpr int QW = Shape::QW, BM = Shape::BM, NT = Shape::NT;
@@ -425,7 +438,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   T* smem = (T*)smem_raw;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
   const size_t C = 2 * DK + DV;
   const T* Qg = qkv + (size_t)bh * C * N;
@@ -451,9 +464,8 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
       for (int cc = 0; cc < CC; ++cc)
         frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
       const int i = i0 + row0 + t;
-      const float2 q = (i < N) ? stats[(size_t)bh * N + i] : make_float2(kPosInf, 0.f);
-      nl[nb] = -q.x;
-      nd[nb] = -q.y;
+      nl[nb] = i < N ? nlg[(size_t)bh * N + i] : kNegInf;
+      nd[nb] = i < N ? ndg[(size_t)bh * N + i] : 0.f;
     }
     __syncthreads();
   }
@@ -474,11 +486,9 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
     const T* nat = smem + (kt & 1) * BUF;  // K channel-major (fp32: K then V)
     const T* tm = tm_of(nat, sk);          // K then V channels, token-major
     if (kt + 1 < nkt) sk.load(KVg, KVg, N, (kt + 1) * BN, tid);
-    const int j0 = kt * BN;
 
 #pragma unroll
     for (int c2 = 0; c2 < BN / 32; ++c2) {
-      const bool tail = j0 + 32 * c2 + 32 > N;
       f32x4 s[2][QB], dp[2][QB];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -502,14 +512,12 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }
+        // Keys past N are zero rows of K, so whatever dS^T holds for them
+        // adds nothing to dQ: no masking needed.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool dead = tail && (j0 + 32 * c2 + 8 * g + 4 * h + r >= N);
 #pragma unroll
-          for (int nb = 0; nb < QB; ++nb) {
-            const float p = dead ? 0.f : fast_exp2(__builtin_fmaf(s[h][nb][r], c, nl[nb]));
-            dp[h][nb][r] *= p;
-          }
+          for (int nb = 0; nb < QB; ++nb) dp[h][nb][r] *= fast_exp2(__builtin_fmaf(s[h][nb][r], c, nl[nb]));
         }
       }
       // dQ^T += K^T dS^T over this chunk's 32 keys.
@@ -548,20 +556,20 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 // ========================================================= backward kernels
 template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dkdv_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
-    T* __restrict__ dpk, int N, int n_ktiles, float c, float scale) {
+    const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
+    T* __restrict__ dpk, int N, int n_ktiles, int n_blocks, float c, float scale) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM];
-  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, stats, dpk, N, n_ktiles, c, scale,
-                                               xcd_remap(blockIdx.x, gridDim.x), smem);
+  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale,
+                                               xcd_remap(block_id(), n_blocks), smem);
 }
 
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
-    T* __restrict__ dpk, int N, int n_qtiles, float c, float scale) {
+    const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
+    T* __restrict__ dpk, int N, int n_qtiles, int n_blocks, float c, float scale) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[DqShape<T, DK, DV, QB, NW, BN>::SMEM];
-  bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, stats, dpk, N, n_qtiles, c, scale,
-                                             xcd_remap(blockIdx.x, gridDim.x), smem);
+  bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale,
+                                             xcd_remap(block_id(), n_blocks), smem);
 }
 
 // Both backward GEMM chains in one launch: the first n_kblocks workgroups
@@ -571,17 +579,17 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
 // workgroups on its own; both share one LDS allocation.
 template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, bool VECOK>
 __global__ __launch_bounds__(256) PSA_OCCUPANCY void psa_bwd_fused_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float2* __restrict__ stats,
-    T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, float c, float scale) {
+    const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
+    T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale) {
   constexpr int S1 = DkdvShape<T, DK, DV, KB, 4, BMQ>::SMEM, S2 = DqShape<T, DK, DV, QB, 4, BN>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S1 > S2 ? S1 : S2];
-  const int b = blockIdx.x;
+  const int b = block_id();
   if (b < n_kblocks)
-    bwd_dkdv_body<T, DK, DV, KB, 4, BMQ, VECOK>(qkv, dO, stats, dpk, N, n_ktiles, c, scale,
+    bwd_dkdv_body<T, DK, DV, KB, 4, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale,
                                                 xcd_remap(b, n_kblocks), smem);
   else
-    bwd_dq_body<T, DK, DV, QB, 4, BN, VECOK>(qkv, dO, stats, dpk, N, n_qtiles, c, scale,
-                                             xcd_remap(b - n_kblocks, (int)gridDim.x - n_kblocks), smem);
+    bwd_dq_body<T, DK, DV, QB, 4, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale,
+                                             xcd_remap(b - n_kblocks, n_qblocks), smem);
 }
 
 }  // namespace psa
