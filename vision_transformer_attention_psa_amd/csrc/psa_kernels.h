@@ -140,19 +140,21 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
       }
 
       // Online softmax per query column; the 4 lane groups hold the rows.
-      float mt[QB];
+      // Each lane checks only its own 8 rows against the running maximum
+      // plus the slack; the exact column maximum (a reduction over the lane
+      // groups) is formed only when some lane's scores outgrew it.
+      float mx[QB];
       bool grow = false;
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) {
-        float mx = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3]));
-        mx = fmaxf(mx, fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
-        mt[nb] = wave_max4(mx) * c;
-        grow |= mt[nb] > m[nb] + kRescaleSlack;
+        mx[nb] = fmaxf(fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3])),
+                       fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
+        grow |= mx[nb] * c > m[nb] + kRescaleSlack;
       }
       if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) {
-          const float mn = fmaxf(m[nb], mt[nb]);
+          const float mn = fmaxf(m[nb], wave_max4(mx[nb]) * c);
           const float alpha = fast_exp2(m[nb] - mn);
           m[nb] = mn;
           lacc[nb] *= alpha;
