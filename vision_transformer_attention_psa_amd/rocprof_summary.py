@@ -26,12 +26,14 @@ PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
 
 
 def short_name(kernel: str) -> str:
+    """Slot name plus dtype and the kernel's integer template arguments
+    (head dims, then tile parameters), e.g. bwd_main<bf16,64,64,2,64,2,64>."""
     for pat, slot in PSA_SLOTS:
         if pat in kernel:
-            m = re.search(r"I(DF16b|f)(?:Li(\d+)E)?(?:Li(\d+)E)?", kernel)
+            m = re.search(pat + r"I(DF16b|f)((?:Li\d+E)*)", kernel)
             if m:
                 dt = "bf16" if m.group(1) == "DF16b" else "f32"
-                dims = "x".join(d for d in m.groups()[1:] if d)
+                dims = ",".join(re.findall(r"Li(\d+)E", m.group(2)))
                 return f"{slot}<{dt},{dims}>"
             return slot
     return kernel[:60]
