@@ -89,6 +89,30 @@ def test_edge_shapes(dtype, dk, dv, B, H, N):
     assert max(err.values()) <= TOL[dtype], err
 
 
+# More tiles than the GPU holds workgroups at once (two per CU on 256 CUs),
+# so workgroups run in several rounds; ragged and 16-byte-aligned N.
+MANY_TILES = [
+    # (dtype, dk, dv, B, heads, N, sampled slices)
+    (inputs.BF16, 64, 64, 10, 16, 1000, 3),
+    (inputs.BF16, 32, 64, 13, 10, 1003, 3),
+    (inputs.F32, 64, 64, 6, 10, 1000, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,B,H,N,ns", MANY_TILES)
+def test_many_tiles_sampled(dtype, dk, dv, B, H, N, ns):
+    wl = inputs.Workload(f"many_{dtype}_{dk}_{dv}_{B}x{H}_n{N}", B=B, heads=H, H=N, W=1, dk=dk,
+                         dv=dv, dtype=dtype, seed=300 + N)
+    x = inputs.make_inputs(wl)
+    got = run_chained(x)
+    sl = inputs.sample_slices(wl, ns)
+    ref = orc.forward_backward(x.qkv, x.dO, dk, dv, wl.scale, slices=sl)
+    err = errors(wl, got, ref, sl)
+    print(wl.name, {k: f"{v:.2e}" for k, v in err.items()}, flush=True)
+    assert all(np.isfinite(a).all() for a in got)
+    assert max(err.values()) <= TOL[dtype], err
+
+
 def test_peaked_softmax_small():
     """sigma(Q, K) = 3 with dk = 64 (logits spread ~35): the high-resolution
     statistics on a slice the oracle finishes quickly, every element compared."""

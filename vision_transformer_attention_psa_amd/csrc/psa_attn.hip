@@ -46,6 +46,9 @@ int fail(int code, const std::string& msg) {
 #ifndef PSA_BF16_DQ_QB
 #define PSA_BF16_DQ_QB 2
 #endif
+#ifndef PSA_BF16_DQ_BN
+#define PSA_BF16_DQ_BN 64
+#endif
 #ifndef PSA_BWD_SPLIT
 #define PSA_BWD_SPLIT 0  // 1: separate dK/dV and dQ launches (per-pass timing)
 #endif
@@ -56,7 +59,7 @@ template <typename T> struct TilesWide;
 template <> struct TilesWide<psa::bf16> {
   static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = PSA_BF16_FWD_QB, FWD_BN = 64;
   static constexpr int DKDV_KB = PSA_BF16_DKDV_KB, DKDV_BMQ = PSA_BF16_DKDV_BMQ;
-  static constexpr int DQ_QB = PSA_BF16_DQ_QB, DQ_BN = 64;
+  static constexpr int DQ_QB = PSA_BF16_DQ_QB, DQ_BN = PSA_BF16_DQ_BN;
 };
 template <> struct TilesWide<float> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
