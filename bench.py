@@ -28,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "PSA attn bwd TFLOP/s + µs/call (B=16,N=400 & N=6400), % of MFMA peak"
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "highres_n6400_bf16"
 ALSO = ("batched_n400_bf16", "midres_n1600_bf16")
@@ -100,12 +100,18 @@ def device_inputs(torch, x):
     if x.wl.dtype == inputs.BF16:
         q = torch.from_numpy(x.qkv_bits.view(np.int16)).view(torch.bfloat16).cuda()
         g = torch.from_numpy(x.dO_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    elif x.wl.dtype == inputs.F16:
+        q = torch.from_numpy(x.qkv_bits.view(np.float16)).cuda()
+        g = torch.from_numpy(x.dO_bits.view(np.float16)).cuda()
     else:
         q, g = torch.from_numpy(x.qkv).cuda(), torch.from_numpy(x.dO).cuda()
     return q, g
 
 
 def time_workload(torch, wl, steps: int, warmup: int) -> dict:
+    """W untimed warm-up steps, then exactly K timed fwd+bwd steps (no library
+    instrumentation), then K fwd-only and K bwd-only calls back to back for
+    per-call times, then K instrumented steps for per-kernel device times."""
     from vision_transformer_attention_psa_amd import binding, inputs
     x = inputs.make_inputs(wl)
     qkv, dO = device_inputs(torch, x)
@@ -113,33 +119,45 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
     lse = torch.empty((wl.B, wl.heads, wl.N), dtype=torch.float32, device="cuda")
     d = torch.empty_like(qkv)
 
-    def step():
+    def fwd():
         binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+
+    def bwd():
         binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
 
+    binding.psa_attn_timing_enable(False)
     for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    binding.psa_attn_timing_reset()
-    binding.psa_attn_timing_enable(True)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        fwd()
+        bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(steps):
-        ev[k][0].record()
-        binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
-        ev[k][1].record()
-        binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
-        ev[k][2].record()
+    for _ in range(steps):
+        fwd()
+        bwd()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ev[0].record()
+    for _ in range(steps):
+        fwd()
+    ev[1].record()
+    for _ in range(steps):
+        bwd()
+    ev[2].record()
+    torch.cuda.synchronize()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / steps
+    bwd_ms = ev[1].elapsed_time(ev[2]) / steps
+    binding.psa_attn_timing_reset()
+    binding.psa_attn_timing_enable(True)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
     binding.psa_attn_timing_enable(False)
     kern = binding.psa_attn_timing_read()
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     assert torch.isfinite(d.float()).all().item(), "non-finite gradient"
     fl = flops(wl)
-    dt = "bf16" if wl.dtype == inputs.BF16 else "f32"
+    dt = wl.dtype
     peak = PEAK_TFLOPS[dt]
     avg = {k: (ms / n if n else float("nan")) for k, (ms, n) in kern.items()}
     return {
@@ -158,9 +176,9 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
 
 
 def time_workload_graph(torch, wl, steps: int, warmup: int) -> dict:
-    """The same fwd+bwd step captured once into a HIP graph and replayed:
-    per-call GPU time without host launch overhead (what a caller that
-    captures its step sees).  Library timing is off during capture."""
+    """The fwd and the bwd call each captured once into a HIP graph and
+    replayed K times: per-call time without Python/ctypes launch overhead.
+    For kernels shorter than a graph launch the host stays the limit."""
     from vision_transformer_attention_psa_amd import binding, inputs
     x = inputs.make_inputs(wl)
     qkv, dO = device_inputs(torch, x)

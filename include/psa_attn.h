@@ -44,7 +44,8 @@ extern "C" {
 
 typedef enum {
   PSA_F32 = 0,  /* float32 storage, float32 arithmetic                    */
-  PSA_BF16 = 1  /* bfloat16 storage, bf16 MFMA with float32 accumulation  */
+  PSA_BF16 = 1, /* bfloat16 storage, bf16 MFMA with float32 accumulation  */
+  PSA_F16 = 2   /* IEEE half storage, fp16 MFMA with float32 accumulation */
 } psa_dtype_t;
 
 typedef enum {

@@ -74,6 +74,11 @@ EDGE = [
     (inputs.BF16, 64, 64, 1, 1, 520),
     (inputs.BF16, 32, 64, 3, 1, 256),
     (inputs.BF16, 64, 64, 1, 1, 1000),
+    (inputs.F16, 32, 64, 2, 2, 97),
+    (inputs.F16, 32, 32, 1, 3, 200),
+    (inputs.F16, 64, 64, 1, 2, 129),
+    (inputs.F16, 64, 64, 1, 1, 1000),
+    (inputs.F16, 32, 64, 1, 2, 1203),
 ]
 
 
@@ -111,6 +116,22 @@ def test_many_tiles_sampled(dtype, dk, dv, B, H, N, ns):
     print(wl.name, {k: f"{v:.2e}" for k, v in err.items()}, flush=True)
     assert all(np.isfinite(a).all() for a in got)
     assert max(err.values()) <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("name", ["midres_n1600_bf16", "highres_n6400_bf16"])
+def test_f16_workloads_sampled(name):
+    """The two large workloads with IEEE half storage (fp16 MFMA, fp32
+    accumulation): every slice computed, a seeded sample compared."""
+    wl = inputs.WORKLOADS[name]
+    wl = wl.with_(name=name.replace("bf16", "f16"), dtype=inputs.F16)
+    x = inputs.make_inputs(wl)
+    got = run_chained(x)
+    sl = inputs.sample_slices(wl, 2)
+    ref = orc.forward_backward(x.qkv, x.dO, wl.dk, wl.dv, wl.scale, slices=sl)
+    err = errors(wl, got, ref, sl)
+    print(wl.name, {k: f"{v:.2e}" for k, v in err.items()}, flush=True)
+    assert all(np.isfinite(a).all() for a in got)
+    assert max(err.values()) <= TOL[wl.dtype], err
 
 
 def test_peaked_softmax_small():

@@ -38,6 +38,24 @@ def test_workload_shapes_and_determinism():
             np.testing.assert_array_equal(inputs.bf16_bits_to_f32(a.qkv_bits), a.qkv)
 
 
+def test_f16_rounding_is_ieee_rne():
+    """binary16 patterns of values whose rounding is fixed by IEEE 754:
+    exact values, ties to even, overflow and the smallest subnormal."""
+    vals = np.array([1.0, -2.0, 65504.0, 65519.0, 65520.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11,
+                     2.0 ** -24, 2.0 ** -26, 0.1], dtype=np.float32)
+    want = [0x3C00, 0xC000, 0x7BFF, 0x7BFF, 0x7C00, 0x3C00, 0x3C02, 0x0001, 0x0000, 0x2E66]
+    assert inputs.f16_bits_rne(vals).tolist() == want
+    back = inputs.f16_bits_to_f32(np.array(want, dtype=np.uint16))
+    assert back[0] == 1.0 and back[2] == 65504.0 and np.isinf(back[4]) and back[7] == 2.0 ** -24
+
+
+def test_f16_workload_values_are_representable():
+    wl = inputs.WORKLOADS["batched_n400_bf16"].with_(B=1, dtype=inputs.F16)
+    x = inputs.make_inputs(wl)
+    np.testing.assert_array_equal(inputs.f16_bits_to_f32(x.qkv_bits), x.qkv)
+    np.testing.assert_array_equal(x.qkv.astype(np.float16).astype(np.float32), x.qkv)
+
+
 def test_highres_qk_sigma():
     wl = inputs.WORKLOADS["highres_n6400_bf16"].with_(B=1, heads=1)
     x = inputs.make_inputs(wl)

@@ -14,6 +14,7 @@ from .build import LIB_PATH
 
 PSA_F32 = 0
 PSA_BF16 = 1
+PSA_F16 = 2
 
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
           4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
@@ -113,7 +114,9 @@ def _dtype_code(t) -> int:
         return PSA_F32
     if t.dtype == torch.bfloat16:
         return PSA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return PSA_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _check(fn: str, rc: int) -> None:

@@ -29,8 +29,9 @@ int fail(int code, const std::string& msg) {
 // Tile shapes.  Wide tiles (64 queries per wave in the forward, 32 keys or
 // queries per wave in the backward) reuse each LDS fragment over more MFMAs;
 // small sequences use 16 per wave so that the grid still fills 256 CUs.
-// bf16 fragments take half the registers of fp32 ones.  Defaults can be
-// overridden at build time (-DPSA_BF16_FWD_QB=...) for tuning.
+// 16-bit fragments (bf16, fp16) take half the registers of fp32 ones and
+// share one set of tiles.  Defaults can be overridden at build time
+// (-DPSA_BF16_FWD_QB=...) for tuning.
 #ifndef PSA_BF16_FWD_QB
 #define PSA_BF16_FWD_QB 4
 #endif
@@ -61,6 +62,7 @@ template <> struct TilesWide<psa::bf16> {
   static constexpr int DKDV_KB = PSA_BF16_DKDV_KB, DKDV_BMQ = PSA_BF16_DKDV_BMQ;
   static constexpr int DQ_QB = PSA_BF16_DQ_QB, DQ_BN = PSA_BF16_DQ_BN;
 };
+template <> struct TilesWide<psa::f16> : TilesWide<psa::bf16> {};
 template <> struct TilesWide<float> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
@@ -262,7 +264,10 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   X(PSA_F32, float, 64, 64)     \
   X(PSA_BF16, psa::bf16, 32, 32) \
   X(PSA_BF16, psa::bf16, 32, 64) \
-  X(PSA_BF16, psa::bf16, 64, 64)
+  X(PSA_BF16, psa::bf16, 64, 64) \
+  X(PSA_F16, psa::f16, 32, 32)   \
+  X(PSA_F16, psa::f16, 32, 64)   \
+  X(PSA_F16, psa::f16, 64, 64)
 
 bool supported(int dk, int dv, int dtype) {
 #define X(DT, T, K, V) if (dtype == DT && dk == K && dv == V) return true;
@@ -280,7 +285,8 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Shape/pointer validation shared by both entry points.
 int validate_common(const char* fn, int B, int heads, int N, int dk, int dv, float scale, int dtype) {
-  if (dtype != PSA_F32 && dtype != PSA_BF16) return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": unknown dtype");
+  if (dtype != PSA_F32 && dtype != PSA_BF16 && dtype != PSA_F16)
+    return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": unknown dtype");
   if (B < 1 || heads < 1 || N < 1 || dk < 1 || dv < 1)
     return fail(PSA_ERR_SHAPE, std::string(fn) + ": B, heads, N, dk, dv must all be >= 1");
   if (!std::isfinite(scale) || !(scale > 0.f))
@@ -292,7 +298,7 @@ int validate_common(const char* fn, int B, int heads, int N, int dk, int dv, flo
   if (!supported(dk, dv, dtype)) {
     char buf[160];
     snprintf(buf, sizeof buf, "%s: no compiled instance for dk=%d dv=%d dtype=%s", fn, dk, dv,
-             dtype == PSA_F32 ? "f32" : "bf16");
+             dtype == PSA_F32 ? "f32" : dtype == PSA_BF16 ? "bf16" : "f16");
     return fail(PSA_ERR_UNSUPPORTED, buf);
   }
   return PSA_OK;

@@ -7,11 +7,11 @@
 // need are
 //   frag_ch  : rows = channels, contraction over 32 tokens.  Read straight
 //              from a channel-major LDS tile ([channel][token]).
-//   frag_tok : rows = tokens, contraction over 32 channels.  bf16 reads it
+//   frag_tok : rows = tokens, contraction over 32 channels.  16-bit types read it
 //              from a token-major LDS copy ([token][channel]) that the
 //              staging code writes once per tile (in-register 4x8 block
 //              transpose); fp32 gathers it from the channel-major tile.
-// Both are one 16-byte LDS read per lane for bf16.
+// Both are one 16-byte LDS read per lane for 16-bit types (bf16, fp16).
 //
 // Chaining: a 16x16 fp32 accumulator block holds row 4*g + r of column
 // (lane & 15) in register r.  Score tiles are computed over 32-token chunks
@@ -28,6 +28,8 @@ namespace psa {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -44,15 +46,25 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
 
-template <typename T> constexpr bool is_bf16() { return sizeof(T) == 2; }
+// 16-bit element types (bf16, fp16) share one code path: bf16 and fp16 tiles
+// have the same shapes and layouts and differ only in the MFMA and the
+// conversions.
+template <typename T> constexpr bool is_16bit() { return sizeof(T) == 2; }
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { typedef bf16x8 type; };
+template <> struct Vec8<f16> { typedef f16x8 type; };
 
 // ---------------------------------------------------------------- fragments
 template <typename T> struct Frag;
 template <> struct Frag<float> { float v[8]; };
 template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<f16> { f16x8 v; };
 
 __device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<f16>& a, const Frag<f16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, c, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
 #pragma unroll
@@ -63,6 +75,11 @@ template <typename T> __device__ __forceinline__ Frag<T> ones_frag();
 template <> __device__ __forceinline__ Frag<bf16> ones_frag<bf16>() {
   Frag<bf16> f;
   f.v = bf16x8{(bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f, (bf16)1.f};
+  return f;
+}
+template <> __device__ __forceinline__ Frag<f16> ones_frag<f16>() {
+  Frag<f16> f;
+  f.v = f16x8{(f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f, (f16)1.f};
   return f;
 }
 template <> __device__ __forceinline__ Frag<float> ones_frag<float>() {
@@ -96,17 +113,19 @@ constexpr int tm_elems(int rows, int ldt) { return rows * ldt + 32 * ((rows + 15
 // Rows = tokens row0 + (PERM ? perm_row(lane&15, h) : lane&15); contraction
 // over channels k0 .. k0+31 of a tensor with CV channels (CV % 16 == 0; the
 // upper half of a chunk past CV reads as zero).
-// bf16: token-major tile (see tm_off).  fp32: channel-major tile
+// 16-bit types: token-major tile (see tm_off).  fp32: channel-major tile
 // nat[ch][token], pitch ldn.
-template <int CV, bool PERM>
-__device__ __forceinline__ void frag_tok(Frag<bf16>& f, const bf16* tm, int ldt, const bf16*, int, int row0,
-                                         int h, int k0) {
+template <int CV, bool PERM, typename T>
+__device__ __forceinline__ void frag_tok(Frag<T>& f, const T* tm, int ldt, const T*, int, int row0, int h,
+                                         int k0) {
+  static_assert(is_16bit<T>(), "16-bit element type");
+  typedef typename Vec8<T>::type V8;
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
   const int row = row0 + (PERM ? perm_row(t, h) : t);
   if (CV % 32 == 0 || k0 + 8 * g < CV) {
-    f.v = *(const bf16x8*)(tm + tm_off(row, k0 + 8 * g, ldt));
+    f.v = *(const V8*)(tm + tm_off(row, k0 + 8 * g, ldt));
   } else {
-    f.v = bf16x8{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    f.v = V8{(T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f};
   }
 }
 template <int CV, bool PERM>
@@ -121,9 +140,11 @@ __device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, cons
 }
 
 // Rows = channels ch0 .. ch0+15, contraction over tokens tok0 + 8g .. +7.
-__device__ __forceinline__ void frag_ch(Frag<bf16>& f, const bf16* nat, int ldn, int ch0, int tok0) {
+template <typename T>
+__device__ __forceinline__ void frag_ch(Frag<T>& f, const T* nat, int ldn, int ch0, int tok0) {
+  static_assert(is_16bit<T>(), "16-bit element type");
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  f.v = *(const bf16x8*)(nat + (ch0 + t) * ldn + tok0 + 8 * g);
+  f.v = *(const typename Vec8<T>::type*)(nat + (ch0 + t) * ldn + tok0 + 8 * g);
 }
 __device__ __forceinline__ void frag_ch(Frag<float>& f, const float* nat, int ldn, int ch0, int tok0) {
   const int lane = lane_id(), t = lane & 15, g = lane >> 4;
@@ -138,7 +159,7 @@ __device__ __forceinline__ void frag_ch(Frag<float>& f, const float* nat, int ld
 
 // Empty asm that consumes a fragment: marks it live at this point so that the
 // code computing it is not moved below later control flow.
-__device__ __forceinline__ void pin(const Frag<bf16>& f) { asm volatile("" ::"v"(f.v)); }
+template <typename T> __device__ __forceinline__ void pin(const Frag<T>& f) { asm volatile("" ::"v"(f.v)); }
 __device__ __forceinline__ void pin(const Frag<float>& f) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(f.v[s]));
@@ -154,9 +175,10 @@ __device__ __forceinline__ float wave_max4(float x) {
 }
 
 // Score blocks h = 0, 1 of one 32-token chunk -> B operand over those tokens.
-__device__ __forceinline__ void acc_to_frag(Frag<bf16>& f, const f32x4& a0, const f32x4& a1) {
-  f.v = bf16x8{(bf16)a0[0], (bf16)a0[1], (bf16)a0[2], (bf16)a0[3],
-               (bf16)a1[0], (bf16)a1[1], (bf16)a1[2], (bf16)a1[3]};
+template <typename T>
+__device__ __forceinline__ void acc_to_frag(Frag<T>& f, const f32x4& a0, const f32x4& a1) {
+  static_assert(is_16bit<T>(), "16-bit element type");
+  f.v = typename Vec8<T>::type{(T)a0[0], (T)a0[1], (T)a0[2], (T)a0[3], (T)a1[0], (T)a1[1], (T)a1[2], (T)a1[3]};
 }
 __device__ __forceinline__ void acc_to_frag(Frag<float>& f, const f32x4& a0, const f32x4& a1) {
 #pragma unroll
@@ -175,7 +197,7 @@ constexpr int tm_pitch(int channels) { return channels + 8; }
 // Global -> registers -> LDS for a tile of C channel rows x BT tokens from
 // token j0 (tokens >= N read as zero).  Rows [0, SPLIT) come from src_lo and
 // rows [SPLIT, C) from src_hi, both channel-major with row stride N.
-//   bf16: each thread owns 4-channel x 8-token blocks (four 16-byte loads).
+//   bf16, fp16: each thread owns 4-channel x 8-token blocks (four 16-byte loads).
 //         Rows in [NAT_LO, NAT_HI) go to a channel-major tile
 //         nat[row - NAT_LO][nat_pitch(BT)]; rows in [0, TM_HI) are also
 //         transposed in registers into a token-major tile tm[token][row]
@@ -185,12 +207,10 @@ constexpr int tm_pitch(int channels) { return channels + 8; }
 // VECOK: N is a multiple of the 16-byte vector, so every chunk is aligned and
 // wholly inside or wholly past the row end.
 template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
-struct Stager;
-
-template <int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
-struct Stager<bf16, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
+struct Stager {  // 16-bit element types (the fp32 specialisation follows)
+  static_assert(is_16bit<T>(), "16-bit element type");
   static constexpr int CG = C / 4, TC = BT / 8, NB = CG * TC, PER = (NB + NT - 1) / NT;
-  static constexpr int LDN = nat_pitch<bf16>(BT), LDT = tm_pitch(TM_HI);
+  static constexpr int LDN = nat_pitch<T>(BT), LDT = tm_pitch(TM_HI);
   static constexpr int NAT_ELEMS = (NAT_HI - NAT_LO) * LDN, TM_ELEMS = TM_HI > 0 ? tm_elems(BT, LDT) : 0;
   // Block q: 4 consecutive blocks run along the tokens of one 4-row group
   // (64 contiguous bytes per row in HBM), then the next row group.
@@ -203,7 +223,7 @@ struct Stager<bf16, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
                     NAT_HI % 4 == 0, "tile shape");
   u32x4 r[PER][4];
 
-  __device__ __forceinline__ void load(const bf16* __restrict__ lo, const bf16* __restrict__ hi, int N, int j0,
+  __device__ __forceinline__ void load(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0,
                                        int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -211,12 +231,12 @@ struct Stager<bf16, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
       const int tc = blk_tc(q), cg = blk_cg(q);
       const int j = j0 + 8 * tc;
       const bool live = NB % NT == 0 || q < NB;
-      const bf16* base = 4 * cg < SPLIT ? lo + (size_t)(4 * cg) * N : hi + (size_t)(4 * cg - SPLIT) * N;
+      const T* base = 4 * cg < SPLIT ? lo + (size_t)(4 * cg) * N : hi + (size_t)(4 * cg - SPLIT) * N;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         r[u][i] = u32x4{0u, 0u, 0u, 0u};
         if (!live) continue;
-        const bf16* p = base + (size_t)i * N + j;
+        const T* p = base + (size_t)i * N + j;
         if constexpr (VECOK) {
           if (j < N) r[u][i] = *(const u32x4*)p;
         } else {
@@ -228,7 +248,7 @@ struct Stager<bf16, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
       }
     }
   }
-  __device__ __forceinline__ void store(bf16* nat, bf16* tm, int tid) const {
+  __device__ __forceinline__ void store(T* nat, T* tm, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   constexpr int QE = SQ::NAT_ELEMS + SQ::TM_ELEMS;
   constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
-  constexpr int VROW = is_bf16<T>() ? 0 : DK;  // first V row in the channel-major tile
+  constexpr int VROW = is_16bit<T>() ? 0 : DK;  // first V row in the channel-major tile
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;

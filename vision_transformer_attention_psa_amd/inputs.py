@@ -12,8 +12,9 @@ upstream gradient ``dO`` is ``[B, heads, dv, N]`` in the same orientation.
 
 Recipe: ``numpy.random.Generator(PCG64(seed))`` draws ``qkv`` then ``dO`` as
 float32 standard normals; the high-resolution workload scales the Q and K
-channels by 3.  bf16 workloads round both tensors to bf16 with
-round-to-nearest-even, and those exact values are what every consumer sees.
+channels by 3.  bf16 and fp16 workloads round both tensors to the storage
+type with round-to-nearest-even, and those exact values are what every
+consumer sees.
 """
 from __future__ import annotations
 
@@ -24,6 +25,8 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+F16 = "f16"
+HALF = (BF16, F16)  # 16-bit storage types
 
 
 @dataclasses.dataclass(frozen=True)
@@ -97,13 +100,26 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+def f16_bits_rne(x: np.ndarray) -> np.ndarray:
+    """float32 -> IEEE binary16 bit patterns (uint16), round to nearest even
+    (numpy's float16 conversion), overflow to +-inf."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of binary16 bit patterns to float32."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 @dataclasses.dataclass
 class Inputs:
     """One draw of a workload.
 
     ``qkv``/``dO`` are float32 arrays holding exactly the values the kernels
-    see (already bf16-representable for bf16 workloads); ``qkv_bits`` and
-    ``dO_bits`` hold the uint16 patterns for bf16 workloads, else ``None``.
+    see (already representable in the storage type for 16-bit workloads);
+    ``qkv_bits`` and ``dO_bits`` hold the uint16 patterns for bf16 and fp16
+    workloads, else ``None``.
     """
 
     wl: Workload
@@ -122,6 +138,9 @@ def make_inputs(wl: Workload, seed: int | None = None) -> Inputs:
     if wl.dtype == BF16:
         qb, db = bf16_bits_rne(qkv), bf16_bits_rne(dO)
         return Inputs(wl, bf16_bits_to_f32(qb), bf16_bits_to_f32(db), qb, db)
+    if wl.dtype == F16:
+        qb, db = f16_bits_rne(qkv), f16_bits_rne(dO)
+        return Inputs(wl, f16_bits_to_f32(qb), f16_bits_to_f32(db), qb, db)
     return Inputs(wl, qkv, dO, None, None)
 
 

@@ -30,9 +30,9 @@ def short_name(kernel: str) -> str:
     (head dims, then tile parameters), e.g. bwd_main<bf16,64,64,2,64,2,64>."""
     for pat, slot in PSA_SLOTS:
         if pat in kernel:
-            m = re.search(pat + r"I(DF16b|f)((?:Li\d+E)*)", kernel)
+            m = re.search(pat + r"I(DF16b|DF16_|f)((?:Li\d+E)*)", kernel)
             if m:
-                dt = "bf16" if m.group(1) == "DF16b" else "f32"
+                dt = {"DF16b": "bf16", "DF16_": "f16"}.get(m.group(1), "f32")
                 dims = ",".join(re.findall(r"Li(\d+)E", m.group(2)))
                 return f"{slot}<{dt},{dims}>"
             return slot
