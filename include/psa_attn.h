@@ -88,7 +88,9 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
                  void* d_packed, int B, int heads, int N, int dk, int dv, float scale,
                  int dtype, void* stream);
 
-/* 1 if (dk, dv, dtype) has a compiled instance, else 0.  No GPU access. */
+/* 1 if (dk, dv, dtype) has a compiled instance, else 0.  No GPU access.
+ * Compiled: (dk, dv) in {(32,32), (32,64), (64,64), (64,128), (128,128)} for
+ * every dtype, and (16,16) for PSA_F32. */
 int psa_attn_supported(int dk, int dv, int dtype);
 
 /* Message for the last non-OK status returned on the calling thread

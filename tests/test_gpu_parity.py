@@ -79,6 +79,13 @@ EDGE = [
     (inputs.F16, 64, 64, 1, 2, 129),
     (inputs.F16, 64, 64, 1, 1, 1000),
     (inputs.F16, 32, 64, 1, 2, 1203),
+    # head dims with dk + dv > 128 (halved register and LDS tiles)
+    (inputs.F32, 64, 128, 1, 2, 130),
+    (inputs.F32, 128, 128, 1, 1, 257),
+    (inputs.BF16, 64, 128, 2, 1, 300),
+    (inputs.BF16, 128, 128, 1, 1, 700),
+    (inputs.F16, 128, 128, 1, 2, 97),
+    (inputs.F16, 64, 128, 1, 1, 1000),
 ]
 
 

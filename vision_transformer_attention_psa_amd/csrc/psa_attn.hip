@@ -56,24 +56,30 @@ int fail(int code, const std::string& msg) {
 #ifndef PSA_SMALL_N_MAX
 #define PSA_SMALL_N_MAX 512  // sequences up to this length use the narrow tiles
 #endif
-template <typename T> struct TilesWide;
-template <> struct TilesWide<psa::bf16> {
-  static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = PSA_BF16_FWD_QB, FWD_BN = 64;
-  static constexpr int DKDV_KB = PSA_BF16_DKDV_KB, DKDV_BMQ = PSA_BF16_DKDV_BMQ;
-  static constexpr int DQ_QB = PSA_BF16_DQ_QB, DQ_BN = PSA_BF16_DQ_BN;
+// Head dims with dk + dv > 128 ("wide heads") halve the per-wave register
+// tiles (their accumulators and stationary fragments are twice as large)
+// and the streamed LDS tiles (their rows are twice as long), so that two
+// workgroups still fit one CU.
+template <int DK, int DV> constexpr bool wide_heads() { return DK + DV > 128; }
+
+template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
+  static constexpr bool W = wide_heads<DK, DV>();
+  static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = W ? 2 : PSA_BF16_FWD_QB, FWD_BN = 64;
+  static constexpr int DKDV_KB = W ? 1 : PSA_BF16_DKDV_KB, DKDV_BMQ = W ? 32 : PSA_BF16_DKDV_BMQ;
+  static constexpr int DQ_QB = W ? 1 : PSA_BF16_DQ_QB, DQ_BN = W ? 32 : PSA_BF16_DQ_BN;
 };
-template <> struct TilesWide<psa::f16> : TilesWide<psa::bf16> {};
-template <> struct TilesWide<float> {
+template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = 32;
 };
-template <typename T> struct TilesNarrow {
+template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
+  static constexpr bool W = wide_heads<DK, DV>();
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
-  static constexpr int DKDV_KB = 1, DKDV_BMQ = 64;
-  static constexpr int DQ_QB = 1, DQ_BN = 64;
+  static constexpr int DKDV_KB = 1, DKDV_BMQ = W ? 32 : 64;
+  static constexpr int DQ_QB = 1, DQ_BN = W ? 32 : 64;
 };
-template <> struct TilesNarrow<float> : TilesWide<float> {};
+template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, DK, DV> {};
 
 // ------------------------------------------------------- per-kernel timing
 // Slots: forward; D/LSE preprocessing; the backward GEMM launch (fused dK/dV
@@ -262,12 +268,18 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   X(PSA_F32, float, 32, 32)     \
   X(PSA_F32, float, 32, 64)     \
   X(PSA_F32, float, 64, 64)     \
+  X(PSA_F32, float, 64, 128)    \
+  X(PSA_F32, float, 128, 128)   \
   X(PSA_BF16, psa::bf16, 32, 32) \
   X(PSA_BF16, psa::bf16, 32, 64) \
   X(PSA_BF16, psa::bf16, 64, 64) \
+  X(PSA_BF16, psa::bf16, 64, 128) \
+  X(PSA_BF16, psa::bf16, 128, 128) \
   X(PSA_F16, psa::f16, 32, 32)   \
   X(PSA_F16, psa::f16, 32, 64)   \
-  X(PSA_F16, psa::f16, 64, 64)
+  X(PSA_F16, psa::f16, 64, 64)   \
+  X(PSA_F16, psa::f16, 64, 128)  \
+  X(PSA_F16, psa::f16, 128, 128)
 
 bool supported(int dk, int dv, int dtype) {
 #define X(DT, T, K, V) if (dtype == DT && dk == K && dv == V) return true;
@@ -396,8 +408,8 @@ int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N, 
   hipStream_t st = (hipStream_t)stream;
 #define X(DT, T, K, V)                                                                     \
   if (dtype == DT && dk == K && dv == V)                                                   \
-    return N <= PSA_SMALL_N_MAX ? run_fwd<T, K, V, TilesNarrow<T>>(qkv, o, lse, (int)BH, N, scale, st) \
-                                : run_fwd<T, K, V, TilesWide<T>>(qkv, o, lse, (int)BH, N, scale, st);
+    return N <= PSA_SMALL_N_MAX ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, (int)BH, N, scale, st) \
+                                : run_fwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, (int)BH, N, scale, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, "psa_attn_fwd: no instance");
@@ -426,8 +438,8 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
 #define X(DT, T, K, V)                                                                              \
   if (dtype == DT && dk == K && dv == V)                                                            \
     return N <= PSA_SMALL_N_MAX                                                                     \
-               ? run_bwd<T, K, V, TilesNarrow<T>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st) \
-               : run_bwd<T, K, V, TilesWide<T>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st);
+               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st) \
+               : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, "psa_attn_bwd: no instance");
