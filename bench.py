@@ -217,6 +217,51 @@ def time_workload_graph(torch, wl, steps: int, warmup: int) -> dict:
     return {"fwd_us": fwd_us, "bwd_us": bwd_us, "bwd_tflops": fl["bwd"] / (bwd_us * 1e-6) / 1e12}
 
 
+def time_conv(torch, wl, steps: int, warmup: int) -> dict:
+    """Backward of the block's qkv projection (a 1x1 convolution) at the
+    workload's shape: x [B, heads*dv, N], w [heads*(2dk+dv), heads*dv], dy the
+    packed gradient.  Two GEMMs of 2*B*N*cin*cout flops each."""
+    import numpy as np
+    from vision_transformer_attention_psa_amd import binding, inputs
+    cin, cout = wl.heads * wl.dv, wl.heads * wl.channels
+    ci = inputs.make_conv_inputs(wl.B, cin, cout, wl.N, wl.dtype, seed=wl.seed)
+
+    def dev(a, k):
+        if ci.bits is None:
+            return torch.from_numpy(a).cuda()
+        if wl.dtype == inputs.BF16:
+            return torch.from_numpy(ci.bits[k].view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(ci.bits[k].view(np.float16)).cuda()
+
+    x, w, dy = dev(ci.x, 0), dev(ci.w, 1), dev(ci.dy, 2)
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    binding.psa_attn_timing_enable(False)
+    for _ in range(warmup):
+        binding.conv_bwd(x, w, dy, out=(dx, dw))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        binding.conv_bwd(x, w, dy, out=(dx, dw))
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    binding.psa_attn_timing_reset()
+    binding.psa_attn_timing_enable(True)
+    for _ in range(steps):
+        binding.conv_bwd(x, w, dy, out=(dx, dw))
+    torch.cuda.synchronize()
+    binding.psa_attn_timing_enable(False)
+    kern = binding.psa_attn_timing_read()
+    fl = 2 * 2.0 * wl.B * wl.N * cin * cout
+    peak = PEAK_TFLOPS[wl.dtype]
+    k_us = {k: kern[k][0] / kern[k][1] * 1e3 for k in ("conv_dx", "conv_dw") if kern[k][1]}
+    return {"shape": {"B": wl.B, "cin": cin, "cout": cout, "N": wl.N}, "us_per_call": us,
+            "tflops": fl / (us * 1e-6) / 1e12, "pct_mfma_peak": 100.0 * fl / (us * 1e-6) / 1e12 / peak,
+            "kernel_avg_us": k_us,
+            "kernel_tflops": {k: fl / 2 / (v * 1e-6) / 1e12 for k, v in k_us.items()}}
+
+
 def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
@@ -313,6 +358,9 @@ def main() -> int:
             graph[name] = time_workload_graph(torch, inputs.WORKLOADS[name], args.steps, args.warmup)
             print(f"[bench] graph replay {name}: fwd {graph[name]['fwd_us']:.1f} us, "
                   f"bwd {graph[name]['bwd_us']:.1f} us", file=sys.stderr, flush=True)
+    conv = time_conv(torch, wl, args.steps, args.warmup)
+    print(f"[bench] qkv 1x1-conv backward {conv['shape']}: {conv['us_per_call']:.1f} us, "
+          f"{conv['tflops']:.1f} TFLOP/s, kernels {conv['kernel_avg_us']}", file=sys.stderr, flush=True)
     traffic = load_traffic(wl.name)
     cpu = None
     if args.cpu_budget > 0:
@@ -344,6 +392,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "also": also,
         "graph_replay": graph,
+        "qkv_conv_bwd": conv,
     }
     print(json.dumps(out), flush=True)
     return 0

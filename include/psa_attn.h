@@ -88,6 +88,27 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
                  void* d_packed, int B, int heads, int N, int dk, int dv, float scale,
                  int dtype, void* stream);
 
+/*
+ * Backward of the 1x1 convolution that produces qkv from the block input x
+ * (Conv2dBackward page, struct description, with kh = kw = 1, stride 1, no
+ * padding and g = 1; no bias).  The forward is y[b][co][n] = sum_ci
+ * w[co][ci] x[b][ci][n]; dy is its upstream gradient, e.g. d_packed of
+ * psa_attn_bwd viewed as [B, cout = heads*(2dk+dv), N].
+ *   x   in   [B, cin, N], dtype
+ *   w   in   [cout, cin], dtype
+ *   dy  in   [B, cout, N], dtype
+ *   dx  out  [B, cin, N], dtype:  dx[b][ci][n] = sum_co w[co][ci] dy[b][co][n]
+ *   dw  out  [cout, cin], dtype:  dw[co][ci] = sum_b sum_n dy[b][co][n] x[b][ci][n]
+ * MFMA GEMMs with fp32 accumulation; every output element is written once
+ * and the sum over (b, n) for dw runs in a fixed order, so results are
+ * bitwise reproducible.  cin and cout must be multiples of 128 (else
+ * PSA_ERR_UNSUPPORTED); N is arbitrary.  dx and dw must not overlap the
+ * inputs or each other.  Scratch: when the dw sum is split, S*cout*cin*4
+ * bytes (S <= 64) from the same per-(device, stream) buffer as psa_attn_bwd.
+ */
+int psa_qkv_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin,
+                     int cout, int N, int dtype, void* stream);
+
 /* 1 if (dk, dv, dtype) has a compiled instance, else 0.  No GPU access.
  * Compiled: (dk, dv) in {(32,32), (32,64), (64,64), (64,128), (128,128)} for
  * every dtype, and (16,16) for PSA_F32. */
@@ -107,9 +128,10 @@ int psa_attn_version(void);
  * accumulated per kernel.  Off by default; process-wide, thread-safe.
  * Kernel slots: 0 = forward, 1 = backward preprocess (D, LSE*log2 e),
  * 2 = backward GEMM launch (dK/dV and dQ in one grid), 3 = backward dQ
- * (used only by builds with -DPSA_BWD_SPLIT=1, where slot 2 is dK/dV).
+ * (used only by builds with -DPSA_BWD_SPLIT=1, where slot 2 is dK/dV),
+ * 4 = psa_qkv_conv_bwd dx, 5 = psa_qkv_conv_bwd dw (with its reduction).
  */
-#define PSA_TIMING_SLOTS 4
+#define PSA_TIMING_SLOTS 6
 /* on != 0 enables, 0 disables.  Returns PSA_OK. */
 int psa_attn_timing_enable(int on);
 /* Waits for every recorded launch, then writes min(n, PSA_TIMING_SLOTS)

@@ -19,10 +19,10 @@ PSA_F16 = 2
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
           4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
 
-EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_supported", "psa_last_error",
+EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_qkv_conv_bwd", "psa_attn_supported", "psa_last_error",
            "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
            "psa_attn_timing_reset")
-TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq")
+TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "conv_dx", "conv_dw")
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.psa_attn_fwd.restype = i
     lib.psa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.psa_attn_bwd.restype = i
+    lib.psa_qkv_conv_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.psa_qkv_conv_bwd.restype = i
     lib.psa_attn_supported.argtypes = [i, i, i]
     lib.psa_attn_supported.restype = i
     lib.psa_last_error.argtypes = []
@@ -87,7 +89,7 @@ def psa_attn_timing_reset() -> int:
 
 
 def psa_attn_timing_read() -> dict:
-    """{slot: (total_ms, launches)} for the four kernel slots."""
+    """{slot: (total_ms, launches)} for every kernel slot."""
     n = len(TIMING_SLOTS)
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_longlong * n)()
@@ -127,6 +129,12 @@ def _check(fn: str, rc: int) -> None:
 def _stream(t) -> int:
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def psa_qkv_conv_bwd(x: int, w: int, dy: int, dx: int, dw: int, B: int, cin: int, cout: int, N: int,
+                     dtype: int, stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_qkv_conv_bwd(x, w, dy, dx, dw, B, cin, cout, N, dtype, stream)
 
 
 def _shape(qkv, dk: int, dv: int):
@@ -170,3 +178,29 @@ def bwd(qkv, o, lse, dO, dk: int, dv: int, scale: float, out=None):
                                         d.data_ptr(), B, H, N, dk, dv, float(scale),
                                         _dtype_code(qkv), _stream(qkv)))
     return d
+
+
+def conv_bwd(x, w, dy, out=None):
+    """(dx [B, cin, N], dw [cout, cin]) of the 1x1 convolution y = w x, for
+    x [B, cin, N], w [cout, cin] and dy [B, cout, N] (dy may be a packed
+    gradient [B, heads, 2dk+dv, N]; it is read as [B, cout, N])."""
+    import torch
+    if x.dim() != 3 or w.dim() != 2:
+        raise ValueError("x must be [B, cin, N] and w [cout, cin]")
+    B, cin, N = x.shape
+    cout = w.shape[0]
+    if w.shape[1] != cin or dy.numel() != B * cout * N or dy.shape[0] != B or dy.shape[-1] != N:
+        raise ValueError(f"dy must hold [B, cout, N] = [{B}, {cout}, {N}]; got {tuple(dy.shape)}")
+    for name, t in (("x", x), ("w", w), ("dy", dy)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != x.dtype:
+            raise ValueError("x, w and dy must share one dtype")
+    if out is None:
+        dx = torch.empty_like(x)
+        dw = torch.empty_like(w)
+    else:
+        dx, dw = out
+    _check("psa_qkv_conv_bwd", psa_qkv_conv_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(),
+                                                dw.data_ptr(), B, cin, cout, N, _dtype_code(x), _stream(x)))
+    return dx, dw

@@ -15,6 +15,7 @@
 #include <utility>
 #include <vector>
 
+#include "psa_conv_kernels.h"
 #include "psa_kernels.h"
 
 namespace {
@@ -83,8 +84,9 @@ template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, D
 
 // ------------------------------------------------------- per-kernel timing
 // Slots: forward; D/LSE preprocessing; the backward GEMM launch (fused dK/dV
-// + dQ, or dK/dV alone when split); dQ when split.
-enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3 };
+// + dQ, or dK/dV alone when split); dQ when split; the 1x1-conv backward's
+// dx GEMM; its dw GEMM (with the split reduction).
+enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5 };
 
 struct Timing {
   std::mutex mu;
@@ -259,6 +261,59 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     rc = check_launch("psa_attn_bwd launch");
   }
 #endif
+  return rc;
+}
+
+template <typename T>
+int run_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin, int cout, int N,
+                 hipStream_t st) {
+  constexpr int R = psa::kConvTile;
+  const int n_ntiles = (N + R - 1) / R, n_citiles = cin / R, n_cotiles = cout / R;
+  const long long gx = (long long)B * n_citiles * n_ntiles;
+  if (gx > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: grid too large");
+  int rc;
+  {
+    TimedLaunch tl(K_CONV_DX, st);
+    if (vec_ok<T>(N))
+      hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, true>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
+                         (const T*)dy, (T*)dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
+    else
+      hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, false>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
+                         (const T*)dy, (T*)dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
+    rc = check_launch("psa_qkv_conv_bwd dx launch");
+  }
+  if (rc != PSA_OK) return rc;
+  // dw: the (b, token chunk) sum is split into S ranges so that the tiles
+  // times S fill about two workgroups per CU, with >= 4 chunks per range.
+  constexpr int BT = psa::is_16bit<T>() ? 64 : 32;
+  const long long nchunk = (long long)B * ((N + BT - 1) / BT);
+  const int tiles = n_citiles * n_cotiles;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(PSA_ERR_HIP, "psa_qkv_conv_bwd: device query failed");
+  long long S = (2LL * cus + tiles - 1) / tiles;
+  S = std::min<long long>(S, std::max<long long>(1, nchunk / 4));
+  S = std::max<long long>(1, std::min<long long>(S, 64));
+  float* part = nullptr;
+  if (S > 1) {
+    part = (float*)scratch_for(st, (size_t)S * cout * cin * sizeof(float));
+    if (part == nullptr) return PSA_ERR_NOMEM;
+  }
+  TimedLaunch tl(K_CONV_DW, st);
+  const int gw = (int)(tiles * S);
+  if (vec_ok<T>(N))
+    hipLaunchKernelGGL((psa::psa_conv_dw_kernel<T, true>), dim3((unsigned)gw), dim3(256), 0, st, (const T*)x,
+                       (const T*)dy, (T*)dw, part, B, cin, cout, N, n_citiles, n_cotiles, (int)S, gw);
+  else
+    hipLaunchKernelGGL((psa::psa_conv_dw_kernel<T, false>), dim3((unsigned)gw), dim3(256), 0, st, (const T*)x,
+                       (const T*)dy, (T*)dw, part, B, cin, cout, N, n_citiles, n_cotiles, (int)S, gw);
+  rc = check_launch("psa_qkv_conv_bwd dw launch");
+  if (rc == PSA_OK && S > 1) {
+    const long long n = (long long)cout * cin;
+    hipLaunchKernelGGL((psa::psa_conv_dw_reduce_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)part, (T*)dw, n, (int)S);
+    rc = check_launch("psa_qkv_conv_bwd dw reduce launch");
+  }
   return rc;
 }
 
@@ -443,6 +498,38 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, "psa_attn_bwd: no instance");
+}
+
+int psa_qkv_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin, int cout,
+                     int N, int dtype, void* stream) {
+  g_err.clear();
+  const char* fn = "psa_qkv_conv_bwd";
+  if (!x || !w || !dy || !dx || !dw) return fail(PSA_ERR_NULL, "psa_qkv_conv_bwd: all pointers must be non-NULL");
+  if (B < 1 || cin < 1 || cout < 1 || N < 1) return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: B, cin, cout, N must be >= 1");
+  if (dtype != PSA_F32 && dtype != PSA_BF16 && dtype != PSA_F16)
+    return fail(PSA_ERR_UNSUPPORTED, "psa_qkv_conv_bwd: unknown dtype");
+  if (cin % psa::kConvTile != 0 || cout % psa::kConvTile != 0)
+    return fail(PSA_ERR_UNSUPPORTED, "psa_qkv_conv_bwd: cin and cout must be multiples of 128");
+  const size_t e = elem_size(dtype);
+  if ((size_t)B * cout * N > (size_t)INT32_MAX * 4 || (size_t)B * cin * N > (size_t)INT32_MAX * 4)
+    return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: tensors too large");
+  if (misaligned(x) || misaligned(w) || misaligned(dy) || misaligned(dx) || misaligned(dw))
+    return fail(PSA_ERR_ALIGN, "psa_qkv_conv_bwd: base pointers must be 16-byte aligned");
+  const Range rx{(uintptr_t)x, (uintptr_t)x + (size_t)B * cin * N * e};
+  const Range rw{(uintptr_t)w, (uintptr_t)w + (size_t)cout * cin * e};
+  const Range ry{(uintptr_t)dy, (uintptr_t)dy + (size_t)B * cout * N * e};
+  const Range rdx{(uintptr_t)dx, (uintptr_t)dx + (size_t)B * cin * N * e};
+  const Range rdw{(uintptr_t)dw, (uintptr_t)dw + (size_t)cout * cin * e};
+  for (const Range& out : {rdx, rdw})
+    if (overlap(out, rx) || overlap(out, rw) || overlap(out, ry))
+      return fail(PSA_ERR_ALIAS, "psa_qkv_conv_bwd: dx and dw must not overlap any input");
+  if (overlap(rdx, rdw)) return fail(PSA_ERR_ALIAS, "psa_qkv_conv_bwd: dx and dw must not overlap");
+  int rc;
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == PSA_F32) return run_conv_bwd<float>(x, w, dy, dx, dw, B, cin, cout, N, st);
+  if (dtype == PSA_BF16) return run_conv_bwd<psa::bf16>(x, w, dy, dx, dw, B, cin, cout, N, st);
+  return run_conv_bwd<psa::f16>(x, w, dy, dx, dw, B, cin, cout, N, st);
 }
 
 }  // extern "C"

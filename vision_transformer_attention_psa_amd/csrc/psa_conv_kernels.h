@@ -1,0 +1,205 @@
+// Backward of the 1x1 convolution that produces the packed projection qkv
+// from the block input x (Conv2dBackward page, struct description, in its
+// kh = kw = 1, stride 1, no padding, g = 1 case).  Per batch b:
+//   y[co][n]  = sum_ci w[co][ci] x[ci][n]              (the forward, not built)
+//   dx[ci][n] = sum_co w[co][ci] dy[co][n]              (psa_conv_dx_kernel)
+//   dw[co][ci] = sum_b sum_n dy[co][n] x[ci][n]         (psa_conv_dw_kernel)
+// dy is the packed gradient [B, heads*(2dk+dv), N] that psa_attn_bwd writes.
+// The page accumulates both with atomics into zeroed buffers; here every
+// output element is written once, dw's sum over b and n is split into S
+// fixed ranges whose fp32 partials a third kernel adds in range order, so
+// the results are deterministic.
+//
+// Both GEMMs run on MFMA with 4 waves per workgroup, each owning a 64 x 64
+// output tile (2 x 2 waves: 128 x 128 per workgroup).
+//   dx: contraction over co, which is the slow index of both w and dy, so
+//       both operands are staged token-major (rows ci resp. n, co
+//       contiguous) and read with frag_tok.
+//   dw: contraction over n, the fast index of both dy and x: both tiles are
+//       channel-major and read with frag_ch, as the attention's dV/dK GEMMs.
+#pragma once
+#include "psa_common.h"
+
+namespace psa {
+
+constexpr int kConvTile = 128;  // output rows and columns per workgroup
+
+// ------------------------------------------------------------------- dx
+// Workgroup: batch b, ci tile [ci0, ci0 + 128), token tile [n0, n0 + 128).
+// co is consumed in chunks of KCH (64, fp32: 32) through a double-buffered
+// pair of tiles holding w^T [128 ci][KCH co] and dy^T [128 n][KCH co]
+// (token-major for 16-bit types; fp32 keeps them channel-major and gathers).
+template <typename T, bool VECOK>
+__global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ w, const T* __restrict__ dy,
+                                                          T* __restrict__ dx, int cin, int cout, int N, int n_ntiles,
+                                                          int n_citiles, int n_blocks) {
+  constexpr int KCH = is_16bit<T>() ? 64 : 32, BT = kConvTile, NT = 256;  // fp32 tiles are twice as wide
+  constexpr int KC = KCH / 32;
+  // rows = co (channels of the chunk), tokens = ci (w) or n (dy)
+  using SW = Stager<T, KCH, BT, NT, true, KCH, (is_16bit<T>() ? KCH : 0), 0, (is_16bit<T>() ? 0 : KCH)>;
+  using SY = Stager<T, KCH, BT, NT, VECOK, KCH, (is_16bit<T>() ? KCH : 0), 0, (is_16bit<T>() ? 0 : KCH)>;
+  constexpr int BUF = SW::NAT_ELEMS + SW::TM_ELEMS;  // one operand tile
+  __shared__ __attribute__((aligned(16))) T smem[4 * BUF];
+
+  const int tid = thread_id(), wv = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int blk = xcd_remap(block_id(), n_blocks);
+  const int per_b = n_ntiles * n_citiles;
+  const int b = blk / per_b, r = blk - b * per_b;
+  const int ci0 = (r / n_ntiles) * BT, n0 = (r - (r / n_ntiles) * n_ntiles) * BT;
+  const T* dyb = dy + (size_t)b * cout * N;
+  const int wr = (wv >> 1) * 64, wc = (wv & 1) * 64;  // this wave's rows (ci) and columns (n)
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  SW sw;
+  SY sy;
+  auto stage = [&](int slot) {
+    T* a = smem + slot * 2 * BUF;
+    T* y = a + BUF;
+    sw.store(a, a + SW::NAT_ELEMS, tid);
+    sy.store(y, y + SY::NAT_ELEMS, tid);
+  };
+  sw.load(w, w, cin, ci0, tid);
+  sy.load(dyb, dyb, N, n0, tid);
+  stage(0);
+  __syncthreads();
+
+  const int nch = cout / KCH;
+  for (int k = 0; k < nch; ++k) {
+    const T* a = smem + (k & 1) * 2 * BUF;
+    const T* y = a + BUF;
+    if (k + 1 < nch) {
+      sw.load(w + (size_t)(k + 1) * KCH * cin, w + (size_t)(k + 1) * KCH * cin, cin, ci0, tid);
+      sy.load(dyb + (size_t)(k + 1) * KCH * N, dyb + (size_t)(k + 1) * KCH * N, N, n0, tid);
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      Frag<T> fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        frag_tok<KCH, false>(fa[i], a + SW::NAT_ELEMS, SW::LDT, a, SW::LDN, wr + 16 * i, 0, 32 * kc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        frag_tok<KCH, false>(fb[j], y + SY::NAT_ELEMS, SY::LDT, y, SY::LDN, wc + 16 * j, 0, 32 * kc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
+    }
+    if (k + 1 < nch) stage((k + 1) & 1);
+    __syncthreads();
+  }
+
+  // acc[i][j]: rows ci0 + wr + 16i + 4g + r, column n0 + wc + 16j + t.
+  T* dxb = dx + (size_t)b * cin * N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wc + 16 * j + t;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          dxb[(size_t)(ci0 + wr + 16 * i + 4 * g + rr) * N + n] = from_f32<T>(acc[i][j][rr]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------- dw
+// Workgroup: co tile [co0, co0 + 128), ci tile [ci0, ci0 + 128), and range
+// s of the token chunks: the B * ceil(N / BT) chunks (b-major) are cut into
+// n_splits contiguous ranges.  Tiles: dy [128 co][BT n] and x [128 ci][BT n],
+// channel-major (BT = 64 tokens, 32 for fp32).  With n_splits == 1 the result goes to dw in the storage
+// type, otherwise to part[s] in fp32.
+template <typename T, bool VECOK>
+__global__ __launch_bounds__(256) void psa_conv_dw_kernel(const T* __restrict__ x, const T* __restrict__ dy,
+                                                          T* __restrict__ dw, float* __restrict__ part, int B,
+                                                          int cin, int cout, int N, int n_citiles, int n_cotiles,
+                                                          int n_splits, int n_blocks) {
+  constexpr int BT = is_16bit<T>() ? 64 : 32, R = kConvTile, NT = 256;
+  using ST = Stager<T, R, BT, NT, VECOK, R, 0, 0, R>;  // channel-major only
+  constexpr int BUF = ST::NAT_ELEMS;
+  __shared__ __attribute__((aligned(16))) T smem[4 * BUF];
+
+  const int tid = thread_id(), wv = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int blk = xcd_remap(block_id(), n_blocks);
+  const int tiles = n_citiles * n_cotiles;
+  const int s = blk / tiles, rr0 = blk - s * tiles;
+  const int co0 = (rr0 / n_citiles) * R, ci0 = (rr0 - (rr0 / n_citiles) * n_citiles) * R;
+  const int cpb = (N + BT - 1) / BT, nchunk = B * cpb;
+  const int c0 = (int)((long long)nchunk * s / n_splits), c1 = (int)((long long)nchunk * (s + 1) / n_splits);
+  const int wr = (wv >> 1) * 64, wc = (wv & 1) * 64;  // this wave's rows (co) and columns (ci)
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  ST sa, sb;
+  auto load = [&](int ck) {
+    const int b = ck / cpb, nn = (ck - b * cpb) * BT;
+    const T* yb = dy + ((size_t)b * cout + co0) * N;
+    const T* xb = x + ((size_t)b * cin + ci0) * N;
+    sa.load(yb, yb, N, nn, tid);
+    sb.load(xb, xb, N, nn, tid);
+  };
+  auto stage = [&](int slot) {
+    T* a = smem + slot * 2 * BUF;
+    sa.store(a, nullptr, tid);
+    sb.store(a + BUF, nullptr, tid);
+  };
+  if (c0 < c1) {
+    load(c0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int ck = c0; ck < c1; ++ck) {
+    const T* a = smem + ((ck - c0) & 1) * 2 * BUF;
+    const T* xt = a + BUF;
+    if (ck + 1 < c1) load(ck + 1);
+#pragma unroll
+    for (int kc = 0; kc < BT / 32; ++kc) {
+      Frag<T> fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) frag_ch(fa[i], a, ST::LDN, wr + 16 * i, 32 * kc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) frag_ch(fb[j], xt, ST::LDN, wc + 16 * j, 32 * kc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma(acc[i][j], fa[i], fb[j]);
+    }
+    if (ck + 1 < c1) stage((ck + 1 - c0) & 1);
+    __syncthreads();
+  }
+
+  // acc[i][j]: row co0 + wr + 16i + 4g + r, column ci0 + wc + 16j + t.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t e = (size_t)(co0 + wr + 16 * i + 4 * g + q) * cin + ci0 + wc + 16 * j + t;
+        if (n_splits == 1) dw[e] = from_f32<T>(acc[i][j][q]);
+        else part[(size_t)s * cout * cin + e] = acc[i][j][q];
+      }
+}
+
+// dw = sum over s of part[s], in s order.
+template <typename T>
+__global__ __launch_bounds__(256) void psa_conv_dw_reduce_kernel(const float* __restrict__ part, T* __restrict__ dw,
+                                                                 long long n, int n_splits) {
+  const long long i = (long long)block_id() * 256 + thread_id();
+  if (i >= n) return;
+  float v = part[i];
+  for (int s = 1; s < n_splits; ++s) v += part[(size_t)s * n + i];
+  dw[i] = from_f32<T>(v);
+}
+
+}  // namespace psa

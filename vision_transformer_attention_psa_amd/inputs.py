@@ -152,3 +152,33 @@ def sample_slices(wl: Workload, count: int, seed: int = 0) -> list[int]:
     rng = np.random.Generator(np.random.PCG64(1000 + seed))
     mid = rng.choice(np.arange(1, wl.BH - 1), size=max(0, count - 2), replace=False)
     return sorted({0, wl.BH - 1, *map(int, mid)})
+
+
+@dataclasses.dataclass
+class ConvInputs:
+    """One draw for the 1x1-convolution backward: x [B, cin, N], w [cout, cin]
+    and dy [B, cout, N] as float32 values exactly representable in `dtype`,
+    with the uint16 patterns for 16-bit dtypes (else None)."""
+
+    dtype: str
+    x: np.ndarray
+    w: np.ndarray
+    dy: np.ndarray
+    bits: tuple | None
+
+
+def make_conv_inputs(B: int, cin: int, cout: int, N: int, dtype: str, seed: int) -> ConvInputs:
+    """Standard normals for x and dy and N(0, 1/cin) weights (the usual
+    fan-in scaling), drawn x, w, dy in that order, then rounded like the
+    attention inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, cin, N), dtype=np.float32)
+    w = rng.standard_normal((cout, cin), dtype=np.float32) * np.float32(1.0 / math.sqrt(cin))
+    dy = rng.standard_normal((B, cout, N), dtype=np.float32)
+    if dtype == BF16:
+        bits = tuple(bf16_bits_rne(a) for a in (x, w, dy))
+        return ConvInputs(dtype, *(bf16_bits_to_f32(b) for b in bits), bits)
+    if dtype == F16:
+        bits = tuple(f16_bits_rne(a) for a in (x, w, dy))
+        return ConvInputs(dtype, *(f16_bits_to_f32(b) for b in bits), bits)
+    return ConvInputs(dtype, x, w, dy, None)
