@@ -262,6 +262,65 @@ def time_conv(torch, wl, steps: int, warmup: int) -> dict:
             "kernel_tflops": {k: fl / 2 / (v * 1e-6) / 1e12 for k, v in k_us.items()}}
 
 
+def time_cat(torch, wl, steps: int, warmup: int) -> dict:
+    """Channel-concatenation backward at the workload's feature map: dy is
+    the gradient of a concatenation of two [B, heads*dv, H, W] inputs (bf16 /
+    the workload's dtype); one input's half is copied out (HBM-bound: each
+    element read once and written once).  Then the copy folded into the qkv
+    convolution's backward, whose input is such a concatenation, against the
+    unfolded sequence (convolution backward, then one copy per part)."""
+    from vision_transformer_attention_psa_amd import binding, inputs
+    c = wl.heads * wl.dv
+    tdt = {inputs.F32: torch.float32, inputs.BF16: torch.bfloat16, inputs.F16: torch.float16}[wl.dtype]
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    dy = torch.randn((wl.B, 2 * c, wl.N), generator=g, device="cuda", dtype=torch.float32).to(tdt)
+    dx = torch.empty((wl.B, c, wl.N), device="cuda", dtype=tdt)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    copy = lambda: binding.channel_cat_bwd(dy, c, c, out=dx)
+    us = timed(copy)
+    binding.psa_attn_timing_reset()
+    binding.psa_attn_timing_enable(True)
+    for _ in range(steps):
+        copy()
+    torch.cuda.synchronize()
+    binding.psa_attn_timing_enable(False)
+    kern = binding.psa_attn_timing_read()["cat"]
+    k_us = kern[0] / kern[1] * 1e3
+    nbytes = 2 * dx.numel() * dx.element_size()
+    gbs = nbytes / (k_us * 1e-6) / 1e9
+    # the fold: x = cat(x_0, x_1) of c/2 channels each feeds the qkv convolution
+    cout = wl.heads * wl.channels
+    x = torch.randn((wl.B, c, wl.N), generator=g, device="cuda", dtype=torch.float32).to(tdt)
+    w = (torch.randn((cout, c), generator=g, device="cuda", dtype=torch.float32) / c ** 0.5).to(tdt)
+    cdy = torch.randn((wl.B, cout, wl.N), generator=g, device="cuda", dtype=torch.float32).to(tdt)
+    full, dw = torch.empty_like(x), torch.empty_like(w)
+    parts = [torch.empty((wl.B, c // 2, wl.N), device="cuda", dtype=tdt) for _ in range(2)]
+
+    def unfolded():
+        binding.conv_bwd(x, w, cdy, out=(full, dw))
+        for k, p in enumerate(parts):
+            binding.channel_cat_bwd(full, c // 2, k * (c // 2), out=p)
+
+    folded_us = timed(lambda: binding.conv_cat_bwd(x, w, cdy, [c // 2, c // 2], out=(parts, dw)))
+    unfolded_us = timed(unfolded)
+    return {"copy": {"shape": {"B": wl.B, "channels": 2 * c, "slice": [c, 2 * c], "N": wl.N},
+                     "us_per_call": us, "kernel_avg_us": k_us, "bytes": nbytes, "GB_per_s": gbs,
+                     "frac_hbm_peak": gbs / PEAK_HBM_GBS},
+            "conv_fold": {"parts": [c // 2, c // 2], "folded_us": folded_us, "unfolded_us": unfolded_us}}
+
+
 def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
@@ -361,6 +420,11 @@ def main() -> int:
     conv = time_conv(torch, wl, args.steps, args.warmup)
     print(f"[bench] qkv 1x1-conv backward {conv['shape']}: {conv['us_per_call']:.1f} us, "
           f"{conv['tflops']:.1f} TFLOP/s, kernels {conv['kernel_avg_us']}", file=sys.stderr, flush=True)
+    cat = time_cat(torch, wl, args.steps, args.warmup)
+    print(f"[bench] channel-cat backward {cat['copy']['shape']}: {cat['copy']['kernel_avg_us']:.1f} us, "
+          f"{cat['copy']['GB_per_s']:.0f} GB/s; folded into the conv backward "
+          f"{cat['conv_fold']['folded_us']:.1f} us vs {cat['conv_fold']['unfolded_us']:.1f} us unfolded",
+          file=sys.stderr, flush=True)
     traffic = load_traffic(wl.name)
     cpu = None
     if args.cpu_budget > 0:
@@ -393,6 +457,7 @@ def main() -> int:
         "also": also,
         "graph_replay": graph,
         "qkv_conv_bwd": conv,
+        "channel_cat_bwd": cat,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -109,6 +109,45 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
 int psa_qkv_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin,
                      int cout, int N, int dtype, void* stream);
 
+/*
+ * psa_qkv_conv_bwd for a convolution whose input is a channel concatenation
+ * x = cat(x_0, ..., x_{n_parts-1}) along channels, with the concatenation's
+ * backward folded into the dx epilogue (ChannelCatBackward page, struct
+ * description: the gradient of one concatenated input is its own channel
+ * range of the combined gradient).  Part k owns channels [begin_k, begin_k +
+ * part_channels[k]) of x, begin_k = part_channels[0] + ... +
+ * part_channels[k-1], and receives exactly those rows of dx:
+ *   dx_parts[k]  out  [B, part_channels[k], N], dtype:
+ *                dx_parts[k][b][c][n] = sum_co w[co][begin_k + c] dy[b][co][n]
+ * dx_parts and part_channels are host arrays of n_parts entries (1 <= n_parts
+ * <= 4); each part_channels[k] >= 1 and they add up to cin (any split, not
+ * only multiples of 128).  x is the concatenated input the forward consumed
+ * [B, cin, N]; w, dy, dw, dtype, scratch and determinism are as for
+ * psa_qkv_conv_bwd, which is the n_parts = 1 case.  No part may overlap an
+ * input, dw or another part; each is 16-byte aligned.
+ */
+int psa_qkv_conv_cat_bwd(const void* x, const void* w, const void* dy, void* const* dx_parts,
+                         const int* part_channels, int n_parts, void* dw, int B, int cin, int cout, int N,
+                         int dtype, void* stream);
+
+/*
+ * Channel-concatenation backward on its own (ChannelCatBackward page, struct
+ * description and index mapping): for the combined gradient dy of a
+ * concatenation, one input's gradient is its slice of every outer row,
+ *   dx[n * chunk + e] = dy[n * total + offset + e],   n < n_outer, e < chunk.
+ * Counts are in elements: for inputs [C_k, H, W] concatenated along channels
+ * into [C, H, W] with n_outer = batch, chunk = C_k*H*W, total = C*H*W and
+ * offset = (channels before input k)*H*W.
+ *   dy  in   [n_outer, total], dtype
+ *   dx  out  [n_outer, chunk], dtype; must not overlap dy
+ * Requires n_outer, chunk >= 1, offset >= 0, offset + chunk <= total
+ * (PSA_ERR_SHAPE otherwise) and 16-byte aligned bases.  A pure copy, no
+ * atomics and no scratch; 16-byte vector accesses when chunk, total and
+ * offset are multiples of 16 bytes.
+ */
+int psa_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int total, int offset, int dtype,
+                        void* stream);
+
 /* 1 if (dk, dv, dtype) has a compiled instance, else 0.  No GPU access.
  * Compiled: (dk, dv) in {(32,32), (32,64), (64,64), (64,128), (128,128)} for
  * every dtype, and (16,16) for PSA_F32. */
@@ -123,15 +162,16 @@ int psa_attn_version(void);
 
 /*
  * Per-kernel device timing, for profiling and roofline reporting.  When
- * enabled, every kernel launch inside psa_attn_fwd / psa_attn_bwd is
+ * enabled, every kernel launch inside the compute entry points is
  * bracketed by two hipEvents recorded on the launch stream; durations are
  * accumulated per kernel.  Off by default; process-wide, thread-safe.
  * Kernel slots: 0 = forward, 1 = backward preprocess (D, LSE*log2 e),
  * 2 = backward GEMM launch (dK/dV and dQ in one grid), 3 = backward dQ
  * (used only by builds with -DPSA_BWD_SPLIT=1, where slot 2 is dK/dV),
- * 4 = psa_qkv_conv_bwd dx, 5 = psa_qkv_conv_bwd dw (with its reduction).
+ * 4 = psa_qkv_conv_bwd / psa_qkv_conv_cat_bwd dx, 5 = their dw (with its
+ * reduction), 6 = psa_channel_cat_bwd.
  */
-#define PSA_TIMING_SLOTS 6
+#define PSA_TIMING_SLOTS 7
 /* on != 0 enables, 0 disables.  Returns PSA_OK. */
 int psa_attn_timing_enable(int on);
 /* Waits for every recorded launch, then writes min(n, PSA_TIMING_SLOTS)

@@ -19,10 +19,11 @@ PSA_F16 = 2
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
           4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
 
-EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_qkv_conv_bwd", "psa_attn_supported", "psa_last_error",
+EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_qkv_conv_bwd", "psa_qkv_conv_cat_bwd",
+           "psa_channel_cat_bwd", "psa_attn_supported", "psa_last_error",
            "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
            "psa_attn_timing_reset")
-TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "conv_dx", "conv_dw")
+TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "conv_dx", "conv_dw", "cat")
 
 _lib = None
 
@@ -50,6 +51,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.psa_attn_bwd.restype = i
     lib.psa_qkv_conv_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.psa_qkv_conv_bwd.restype = i
+    lib.psa_qkv_conv_cat_bwd.argtypes = [vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(i), i, vp, i, i, i,
+                                         i, i, vp]
+    lib.psa_qkv_conv_cat_bwd.restype = i
+    lib.psa_channel_cat_bwd.argtypes = [vp, vp, i, i, i, i, i, vp]
+    lib.psa_channel_cat_bwd.restype = i
     lib.psa_attn_supported.argtypes = [i, i, i]
     lib.psa_attn_supported.restype = i
     lib.psa_last_error.argtypes = []
@@ -137,6 +143,22 @@ def psa_qkv_conv_bwd(x: int, w: int, dy: int, dx: int, dw: int, B: int, cin: int
     return load().psa_qkv_conv_bwd(x, w, dy, dx, dw, B, cin, cout, N, dtype, stream)
 
 
+def psa_qkv_conv_cat_bwd(x: int, w: int, dy: int, dx_parts, part_channels, dw: int, B: int, cin: int,
+                         cout: int, N: int, dtype: int, stream: int | None) -> int:
+    """Raw call; dx_parts (device addresses) and part_channels are Python
+    sequences of equal length.  Returns the status code."""
+    n = len(dx_parts)
+    ptrs = (ctypes.c_void_p * max(1, n))(*dx_parts)
+    chans = (ctypes.c_int * max(1, len(part_channels)))(*part_channels)
+    return load().psa_qkv_conv_cat_bwd(x, w, dy, ptrs, chans, n, dw, B, cin, cout, N, dtype, stream)
+
+
+def psa_channel_cat_bwd(dy: int, dx: int, n_outer: int, chunk: int, total: int, offset: int, dtype: int,
+                        stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_channel_cat_bwd(dy, dx, n_outer, chunk, total, offset, dtype, stream)
+
+
 def _shape(qkv, dk: int, dv: int):
     if qkv.dim() != 4 or qkv.shape[2] != 2 * dk + dv:
         raise ValueError(f"qkv must be [B, heads, 2*dk+dv, N]; got {tuple(qkv.shape)}")
@@ -204,3 +226,48 @@ def conv_bwd(x, w, dy, out=None):
     _check("psa_qkv_conv_bwd", psa_qkv_conv_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(),
                                                 dw.data_ptr(), B, cin, cout, N, _dtype_code(x), _stream(x)))
     return dx, dw
+
+
+def conv_cat_bwd(x, w, dy, part_channels, out=None):
+    """([dx_k [B, c_k, N] for each part], dw [cout, cin]) of y = w cat(x_0, ...)
+    for the concatenated input x [B, cin, N]; sum(part_channels) == cin."""
+    import torch
+    if x.dim() != 3 or w.dim() != 2:
+        raise ValueError("x must be [B, cin, N] and w [cout, cin]")
+    B, cin, N = x.shape
+    cout = w.shape[0]
+    if w.shape[1] != cin or dy.numel() != B * cout * N or dy.shape[0] != B or dy.shape[-1] != N:
+        raise ValueError(f"dy must hold [B, cout, N] = [{B}, {cout}, {N}]; got {tuple(dy.shape)}")
+    for name, t in (("x", x), ("w", w), ("dy", dy)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != x.dtype:
+            raise ValueError("x, w and dy must share one dtype")
+    if out is None:
+        dxs = [torch.empty((B, c, N), dtype=x.dtype, device=x.device) for c in part_channels]
+        dw = torch.empty_like(w)
+    else:
+        dxs, dw = out
+    _check("psa_qkv_conv_cat_bwd",
+           psa_qkv_conv_cat_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), [d.data_ptr() for d in dxs],
+                                list(part_channels), dw.data_ptr(), B, cin, cout, N, _dtype_code(x),
+                                _stream(x)))
+    return dxs, dw
+
+
+def channel_cat_bwd(dy, channels: int, offset: int, out=None):
+    """dx [B, channels, *spatial] = dy[:, offset:offset + channels] for a
+    contiguous channel-concatenated gradient dy [B, C, *spatial]."""
+    import torch
+    if dy.dim() < 2 or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous [B, C, ...] tensor")
+    B, C = dy.shape[0], dy.shape[1]
+    inner = dy[0, 0].numel()
+    shape = (B, channels, *dy.shape[2:])
+    dx = torch.empty(shape, dtype=dy.dtype, device=dy.device) if out is None else out
+    if tuple(dx.shape) != shape or dx.dtype != dy.dtype or not dx.is_contiguous():
+        raise ValueError(f"out must be a contiguous {shape} tensor of dy's dtype")
+    _check("psa_channel_cat_bwd", psa_channel_cat_bwd(dy.data_ptr(), dx.data_ptr(), B, channels * inner,
+                                                      C * inner, offset * inner, _dtype_code(dy),
+                                                      _stream(dy)))
+    return dx

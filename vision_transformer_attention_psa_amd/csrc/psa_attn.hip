@@ -85,8 +85,8 @@ template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, D
 // ------------------------------------------------------- per-kernel timing
 // Slots: forward; D/LSE preprocessing; the backward GEMM launch (fused dK/dV
 // + dQ, or dK/dV alone when split); dQ when split; the 1x1-conv backward's
-// dx GEMM; its dw GEMM (with the split reduction).
-enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5 };
+// dx GEMM; its dw GEMM (with the split reduction); the channel-cat slice copy.
+enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5, K_CAT = 6 };
 
 struct Timing {
   std::mutex mu;
@@ -265,8 +265,8 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
 }
 
 template <typename T>
-int run_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin, int cout, int N,
-                 hipStream_t st) {
+int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxParts<T>& dx, void* dw, int B, int cin,
+                 int cout, int N, hipStream_t st) {
   constexpr int R = psa::kConvTile;
   const int n_ntiles = (N + R - 1) / R, n_citiles = cin / R, n_cotiles = cout / R;
   const long long gx = (long long)B * n_citiles * n_ntiles;
@@ -276,10 +276,10 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* d
     TimedLaunch tl(K_CONV_DX, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, true>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
-                         (const T*)dy, (T*)dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
+                         (const T*)dy, dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
     else
       hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, false>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
-                         (const T*)dy, (T*)dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
+                         (const T*)dy, dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
     rc = check_launch("psa_qkv_conv_bwd dx launch");
   }
   if (rc != PSA_OK) return rc;
@@ -315,6 +315,25 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* d
     rc = check_launch("psa_qkv_conv_bwd dw reduce launch");
   }
   return rc;
+}
+
+template <typename T>
+int run_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int total, int offset, hipStream_t st) {
+  constexpr int V = 16 / (int)sizeof(T);
+  const bool vec = chunk % V == 0 && total % V == 0 && offset % V == 0;
+  const long long per_vec = 256LL * psa::kCatUnroll;
+  const long long units = vec ? chunk / V : chunk;
+  const long long per_row = (units + per_vec - 1) / per_vec;
+  const long long grid = per_row * n_outer;
+  if (grid > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_channel_cat_bwd: grid too large");
+  TimedLaunch tl(K_CAT, st);
+  if (vec)
+    hipLaunchKernelGGL((psa::psa_channel_cat_bwd_kernel<T, true>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const T*)dy, (T*)dx, (long long)chunk, (long long)total, (long long)offset, (int)per_row);
+  else
+    hipLaunchKernelGGL((psa::psa_channel_cat_bwd_kernel<T, false>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const T*)dy, (T*)dx, (long long)chunk, (long long)total, (long long)offset, (int)per_row);
+  return check_launch("psa_channel_cat_bwd launch");
 }
 
 // ------------------------------------------------------------ instance table
@@ -389,6 +408,69 @@ int check_device(const char* fn) {
   }
   if (known[dev] != 1) return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": device is not gfx950");
   return PSA_OK;
+}
+
+int conv_bwd_impl(const char* fn, const void* x, const void* w, const void* dy, void* const* dx_parts,
+                  const int* part_channels, int n_parts, void* dw, int B, int cin, int cout, int N, int dtype,
+                  void* stream) {
+  g_err.clear();
+  if (!x || !w || !dy || !dw || !dx_parts || !part_channels)
+    return fail(PSA_ERR_NULL, std::string(fn) + ": all pointers must be non-NULL");
+  if (n_parts < 1 || n_parts > psa::kCatMaxParts)
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": n_parts must be in [1, 4]");
+  if (B < 1 || cin < 1 || cout < 1 || N < 1) return fail(PSA_ERR_SHAPE, std::string(fn) + ": B, cin, cout, N must be >= 1");
+  if (dtype != PSA_F32 && dtype != PSA_BF16 && dtype != PSA_F16)
+    return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": unknown dtype");
+  if (cin % psa::kConvTile != 0 || cout % psa::kConvTile != 0)
+    return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": cin and cout must be multiples of 128");
+  const size_t e = elem_size(dtype);
+  if ((size_t)B * cout * N > (size_t)INT32_MAX * 4 || (size_t)B * cin * N > (size_t)INT32_MAX * 4)
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": tensors too large");
+  long long csum = 0;
+  for (int k = 0; k < n_parts; ++k) {
+    if (!dx_parts[k]) return fail(PSA_ERR_NULL, std::string(fn) + ": all pointers must be non-NULL");
+    if (part_channels[k] < 1) return fail(PSA_ERR_SHAPE, std::string(fn) + ": every part needs >= 1 channel");
+    csum += part_channels[k];
+  }
+  if (csum != cin) return fail(PSA_ERR_SHAPE, std::string(fn) + ": part channels must add up to cin");
+  if (misaligned(x) || misaligned(w) || misaligned(dy) || misaligned(dw))
+    return fail(PSA_ERR_ALIGN, std::string(fn) + ": base pointers must be 16-byte aligned");
+  for (int k = 0; k < n_parts; ++k)
+    if (misaligned(dx_parts[k])) return fail(PSA_ERR_ALIGN, std::string(fn) + ": base pointers must be 16-byte aligned");
+  const Range rx{(uintptr_t)x, (uintptr_t)x + (size_t)B * cin * N * e};
+  const Range rw{(uintptr_t)w, (uintptr_t)w + (size_t)cout * cin * e};
+  const Range ry{(uintptr_t)dy, (uintptr_t)dy + (size_t)B * cout * N * e};
+  const Range rdw{(uintptr_t)dw, (uintptr_t)dw + (size_t)cout * cin * e};
+  Range outs[psa::kCatMaxParts + 1];
+  outs[0] = rdw;
+  for (int k = 0; k < n_parts; ++k)
+    outs[k + 1] = Range{(uintptr_t)dx_parts[k], (uintptr_t)dx_parts[k] + (size_t)B * part_channels[k] * N * e};
+  for (int k = 0; k <= n_parts; ++k) {
+    if (overlap(outs[k], rx) || overlap(outs[k], rw) || overlap(outs[k], ry))
+      return fail(PSA_ERR_ALIAS, std::string(fn) + ": outputs must not overlap any input");
+    for (int q = 0; q < k; ++q)
+      if (overlap(outs[k], outs[q])) return fail(PSA_ERR_ALIAS, std::string(fn) + ": outputs must not overlap");
+  }
+  int rc;
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  auto go = [&](auto tag) {
+    using T = decltype(tag);
+    psa::DxParts<T> parts{};
+    int first = 0;
+    for (int k = 0; k < psa::kCatMaxParts; ++k) {
+      const int kk = k < n_parts ? k : n_parts - 1;  // unused slots repeat the last part
+      parts.p[k] = (T*)dx_parts[kk];
+      parts.begin[k] = k < n_parts ? first : parts.begin[kk];
+      parts.ch[k] = part_channels[kk];
+      if (k < n_parts) first += part_channels[k];
+    }
+    parts.n = n_parts;
+    return run_conv_bwd<T>(x, w, dy, parts, dw, B, cin, cout, N, st);
+  };
+  if (dtype == PSA_F32) return go(float{});
+  if (dtype == PSA_BF16) return go(psa::bf16{});
+  return go(psa::f16{});
 }
 
 }  // namespace
@@ -502,34 +584,39 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
 
 int psa_qkv_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin, int cout,
                      int N, int dtype, void* stream) {
+  void* parts[1] = {dx};
+  const int ch[1] = {cin};
+  return conv_bwd_impl("psa_qkv_conv_bwd", x, w, dy, parts, ch, 1, dw, B, cin, cout, N, dtype, stream);
+}
+
+int psa_qkv_conv_cat_bwd(const void* x, const void* w, const void* dy, void* const* dx_parts,
+                         const int* part_channels, int n_parts, void* dw, int B, int cin, int cout, int N, int dtype,
+                         void* stream) {
+  return conv_bwd_impl("psa_qkv_conv_cat_bwd", x, w, dy, dx_parts, part_channels, n_parts, dw, B, cin, cout, N,
+                       dtype, stream);
+}
+
+int psa_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int total, int offset, int dtype,
+                        void* stream) {
   g_err.clear();
-  const char* fn = "psa_qkv_conv_bwd";
-  if (!x || !w || !dy || !dx || !dw) return fail(PSA_ERR_NULL, "psa_qkv_conv_bwd: all pointers must be non-NULL");
-  if (B < 1 || cin < 1 || cout < 1 || N < 1) return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: B, cin, cout, N must be >= 1");
+  const char* fn = "psa_channel_cat_bwd";
+  if (!dy || !dx) return fail(PSA_ERR_NULL, "psa_channel_cat_bwd: dy and dx must be non-NULL");
   if (dtype != PSA_F32 && dtype != PSA_BF16 && dtype != PSA_F16)
-    return fail(PSA_ERR_UNSUPPORTED, "psa_qkv_conv_bwd: unknown dtype");
-  if (cin % psa::kConvTile != 0 || cout % psa::kConvTile != 0)
-    return fail(PSA_ERR_UNSUPPORTED, "psa_qkv_conv_bwd: cin and cout must be multiples of 128");
+    return fail(PSA_ERR_UNSUPPORTED, "psa_channel_cat_bwd: unknown dtype");
+  if (n_outer < 1 || chunk < 1 || offset < 0 || total < 1 || (long long)offset + chunk > total)
+    return fail(PSA_ERR_SHAPE, "psa_channel_cat_bwd: need n_outer, chunk >= 1, offset >= 0, offset + chunk <= total");
+  if (misaligned(dy) || misaligned(dx))
+    return fail(PSA_ERR_ALIGN, "psa_channel_cat_bwd: base pointers must be 16-byte aligned");
   const size_t e = elem_size(dtype);
-  if ((size_t)B * cout * N > (size_t)INT32_MAX * 4 || (size_t)B * cin * N > (size_t)INT32_MAX * 4)
-    return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: tensors too large");
-  if (misaligned(x) || misaligned(w) || misaligned(dy) || misaligned(dx) || misaligned(dw))
-    return fail(PSA_ERR_ALIGN, "psa_qkv_conv_bwd: base pointers must be 16-byte aligned");
-  const Range rx{(uintptr_t)x, (uintptr_t)x + (size_t)B * cin * N * e};
-  const Range rw{(uintptr_t)w, (uintptr_t)w + (size_t)cout * cin * e};
-  const Range ry{(uintptr_t)dy, (uintptr_t)dy + (size_t)B * cout * N * e};
-  const Range rdx{(uintptr_t)dx, (uintptr_t)dx + (size_t)B * cin * N * e};
-  const Range rdw{(uintptr_t)dw, (uintptr_t)dw + (size_t)cout * cin * e};
-  for (const Range& out : {rdx, rdw})
-    if (overlap(out, rx) || overlap(out, rw) || overlap(out, ry))
-      return fail(PSA_ERR_ALIAS, "psa_qkv_conv_bwd: dx and dw must not overlap any input");
-  if (overlap(rdx, rdw)) return fail(PSA_ERR_ALIAS, "psa_qkv_conv_bwd: dx and dw must not overlap");
+  const Range ry{(uintptr_t)dy, (uintptr_t)dy + (size_t)n_outer * total * e};
+  const Range rx{(uintptr_t)dx, (uintptr_t)dx + (size_t)n_outer * chunk * e};
+  if (overlap(rx, ry)) return fail(PSA_ERR_ALIAS, "psa_channel_cat_bwd: dx must not overlap dy");
   int rc;
   if ((rc = check_device(fn)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == PSA_F32) return run_conv_bwd<float>(x, w, dy, dx, dw, B, cin, cout, N, st);
-  if (dtype == PSA_BF16) return run_conv_bwd<psa::bf16>(x, w, dy, dx, dw, B, cin, cout, N, st);
-  return run_conv_bwd<psa::f16>(x, w, dy, dx, dw, B, cin, cout, N, st);
+  if (dtype == PSA_F32) return run_channel_cat_bwd<float>(dy, dx, n_outer, chunk, total, offset, st);
+  if (dtype == PSA_BF16) return run_channel_cat_bwd<psa::bf16>(dy, dx, n_outer, chunk, total, offset, st);
+  return run_channel_cat_bwd<psa::f16>(dy, dx, n_outer, chunk, total, offset, st);
 }
 
 }  // extern "C"

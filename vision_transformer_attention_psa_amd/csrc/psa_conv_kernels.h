@@ -18,6 +18,8 @@
 //   dw: contraction over n, the fast index of both dy and x: both tiles are
 //       channel-major and read with frag_ch, as the attention's dV/dK GEMMs.
 #pragma once
+#include <type_traits>
+
 #include "psa_common.h"
 
 namespace psa {
@@ -29,10 +31,26 @@ constexpr int kConvTile = 128;  // output rows and columns per workgroup
 // co is consumed in chunks of KCH (64, fp32: 32) through a double-buffered
 // pair of tiles holding w^T [128 ci][KCH co] and dy^T [128 n][KCH co]
 // (token-major for 16-bit types; fp32 keeps them channel-major and gathers).
+//
+// Channel-cat fold (ChannelCatBackward page, struct description): when x is
+// the channel concatenation of up to kCatMaxParts inputs, x = cat(x_0, ...),
+// the gradient of input k is rows [begin_k, begin_k + ch_k) of dx.  The
+// epilogue writes each row straight into its input's own [B, ch_k, N]
+// buffer instead of materialising dx and slicing it afterwards.  A plain dx
+// is the one-part case.
+constexpr int kCatMaxParts = 4;
+template <typename T>
+struct DxParts {
+  T* p[kCatMaxParts];
+  int begin[kCatMaxParts];  // first channel of each part, ascending; begin[0] = 0
+  int ch[kCatMaxParts];     // channels of each part
+  int n;                    // parts in use, 1..kCatMaxParts
+};
+
 template <typename T, bool VECOK>
 __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ w, const T* __restrict__ dy,
-                                                          T* __restrict__ dx, int cin, int cout, int N, int n_ntiles,
-                                                          int n_citiles, int n_blocks) {
+                                                          const DxParts<T> parts, int cin, int cout, int N,
+                                                          int n_ntiles, int n_citiles, int n_blocks) {
   constexpr int KCH = is_16bit<T>() ? 64 : 32, BT = kConvTile, NT = 256;  // fp32 tiles are twice as wide
   constexpr int KC = KCH / 32;
   // rows = co (channels of the chunk), tokens = ci (w) or n (dy)
@@ -95,18 +113,29 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
   }
 
   // acc[i][j]: rows ci0 + wr + 16i + 4g + r, column n0 + wc + 16j + t.
-  T* dxb = dx + (size_t)b * cin * N;
+  // Each row's part is picked with selects (no dynamic index into the
+  // kernel-argument struct).
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wc + 16 * j + t;
-    if (n < N) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int rr = 0; rr < 4; ++rr) {
+      const int ci = ci0 + wr + 16 * i + 4 * g + rr;
+      T* base = parts.p[0];
+      int first = 0, ch = parts.ch[0];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          dxb[(size_t)(ci0 + wr + 16 * i + 4 * g + rr) * N + n] = from_f32<T>(acc[i][j][rr]);
+      for (int q = 1; q < kCatMaxParts; ++q)
+        if (q < parts.n && ci >= parts.begin[q]) {
+          base = parts.p[q];
+          first = parts.begin[q];
+          ch = parts.ch[q];
+        }
+      T* row = base + ((size_t)b * ch + (ci - first)) * N;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wc + 16 * j + t;
+        if (n < N) row[n] = from_f32<T>(acc[i][j][rr]);
+      }
     }
-  }
 }
 
 // ------------------------------------------------------------------- dw
@@ -200,6 +229,39 @@ __global__ __launch_bounds__(256) void psa_conv_dw_reduce_kernel(const float* __
   float v = part[i];
   for (int s = 1; s < n_splits; ++s) v += part[(size_t)s * n + i];
   dw[i] = from_f32<T>(v);
+}
+
+// ------------------------------------------------------- channel-cat backward
+// ChannelCatBackward page, struct description: one input's gradient is its
+// slice of the concatenated upstream gradient.  Per outer index n (the
+// batch), dx holds chunk contiguous elements and dy holds total, of which
+// the input's are [off, off + chunk):
+//   dx[n * chunk + e] = dy[n * total + off + e],  e < chunk.
+// (For a channel concatenation of [C_k, H, W] tensors, chunk = C_k*H*W and
+// off = (channels before input k)*H*W.)  Workgroup blk copies segment
+// blk % per_row (256 * kCatUnroll vectors) of run n = blk / per_row, in
+// 16-byte vectors when chunk, total and off are multiples of 16 bytes,
+// else element by element.
+constexpr int kCatUnroll = 4;  // vectors (or elements) per thread
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void psa_channel_cat_bwd_kernel(const T* __restrict__ dy, T* __restrict__ dx,
+                                                                  long long run, long long dy_row, long long off,
+                                                                  int per_row) {
+  constexpr int V = VEC ? 16 / (int)sizeof(T) : 1;
+  typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+  using Vec = typename std::conditional<VEC, u32x4v, T>::type;
+  const int blk = block_id(), n = blk / per_row, seg = blk - n * per_row;
+  const Vec* src = (const Vec*)(dy + (size_t)n * dy_row + off);
+  Vec* dst = (Vec*)(dx + (size_t)n * run);
+  const long long nv = run / V, k0 = (long long)seg * 256 * kCatUnroll + thread_id();
+  Vec r[kCatUnroll];
+#pragma unroll
+  for (int u = 0; u < kCatUnroll; ++u)
+    if (k0 + u * 256 < nv) r[u] = src[k0 + u * 256];
+#pragma unroll
+  for (int u = 0; u < kCatUnroll; ++u)
+    if (k0 + u * 256 < nv) dst[k0 + u * 256] = r[u];
 }
 
 }  // namespace psa
