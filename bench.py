@@ -321,6 +321,47 @@ def time_cat(torch, wl, steps: int, warmup: int) -> dict:
             "conv_fold": {"parts": [c // 2, c // 2], "folded_us": folded_us, "unfolded_us": unfolded_us}}
 
 
+def time_lohi(torch, wl, steps: int, warmup: int) -> dict | None:
+    """The two-call pattern (one attention call per half of V, merge, merge
+    backward, two accumulating backward calls) at the workload's shape, next
+    to the single call over all of V that computes the same results."""
+    from vision_transformer_attention_psa_amd import binding, inputs
+    h = wl.dv // 2
+    code = {inputs.F32: binding.PSA_F32, inputs.BF16: binding.PSA_BF16, inputs.F16: binding.PSA_F16}[wl.dtype]
+    if not binding.psa_attn_supported(wl.dk, h, code):
+        return None
+    qkv, dO = device_inputs(torch, inputs.make_inputs(wl))
+    o_lo, l_lo = binding.fwd_vslice(qkv, wl.dk, wl.dv, 0, h, wl.scale)
+    o_hi, l_hi = binding.fwd_vslice(qkv, wl.dk, wl.dv, h, wl.dv - h, wl.scale)
+    merged = binding.merge_fwd(o_lo, o_hi)
+    g_lo, g_hi = binding.merge_bwd(dO)
+    d = torch.empty_like(qkv)
+
+    def fwd():
+        binding.fwd_vslice(qkv, wl.dk, wl.dv, 0, h, wl.scale, out=(o_lo, l_lo))
+        binding.fwd_vslice(qkv, wl.dk, wl.dv, h, wl.dv - h, wl.scale, out=(o_hi, l_hi))
+        binding.merge_fwd(o_lo, o_hi, out=merged)
+
+    def bwd():
+        binding.merge_bwd(dO, out=(g_lo, g_hi))
+        binding.bwd_vslice(qkv, o_lo, l_lo, g_lo, d, wl.dk, wl.dv, 0, h, wl.scale, accumulate=False)
+        binding.bwd_vslice(qkv, o_hi, l_hi, g_hi, d, wl.dk, wl.dv, h, wl.dv - h, wl.scale, accumulate=True)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    return {"halves": [h, wl.dv - h], "fwd_us": timed(fwd), "bwd_us": timed(bwd)}
+
+
 def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
@@ -425,6 +466,11 @@ def main() -> int:
           f"{cat['copy']['GB_per_s']:.0f} GB/s; folded into the conv backward "
           f"{cat['conv_fold']['folded_us']:.1f} us vs {cat['conv_fold']['unfolded_us']:.1f} us unfolded",
           file=sys.stderr, flush=True)
+    lohi = time_lohi(torch, wl, args.steps, args.warmup)
+    if lohi:
+        print(f"[bench] lo/hi two-call pattern (halves {lohi['halves']}): fwd {lohi['fwd_us']:.1f} us, "
+              f"bwd {lohi['bwd_us']:.1f} us (one call: fwd {r['fwd_us']:.1f}, bwd {r['bwd_us']:.1f})",
+              file=sys.stderr, flush=True)
     traffic = load_traffic(wl.name)
     cpu = None
     if args.cpu_budget > 0:
@@ -458,6 +504,7 @@ def main() -> int:
         "graph_replay": graph,
         "qkv_conv_bwd": conv,
         "channel_cat_bwd": cat,
+        "lo_hi_two_call": lohi,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -89,6 +89,60 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
                  int dtype, void* stream);
 
 /*
+ * The same forward over a slice of V: rows [v0, v0 + dv) of the V section
+ * of a packed buffer whose slices hold 2dk + dv_total channels.  This is the
+ * call pattern of the PsaFa2Backward page, which runs one attention call per
+ * half of V ("lo" and "hi") over the same Q and K; P, and so LSE, are the
+ * same for every slice.
+ *   qkv  in   [B, heads, 2dk+dv_total, N], dtype
+ *   o    out  [B, heads, dv, N], dtype: P V[:, v0:v0+dv]
+ *   lse  out  [B, heads, N], float32
+ * Requires 0 <= v0 and v0 + dv <= dv_total (else PSA_ERR_SHAPE); (dk, dv)
+ * must have a compiled instance.  psa_attn_fwd is the case v0 = 0,
+ * dv = dv_total.  Scratch: none.
+ */
+int psa_attn_fwd_vslice(const void* qkv, void* o, float* lse, int B, int heads, int N, int dk, int dv_total,
+                        int v0, int dv, float scale, int dtype, void* stream);
+
+/*
+ * The backward of one V-slice call (PsaFa2Backward page: each call owns its
+ * V section of d_packed, and the calls share the dQ and dK sections).
+ *   qkv, lse   as for psa_attn_fwd_vslice
+ *   o, dO      in   [B, heads, dv, N], dtype: this slice's output and its
+ *                   upstream gradient (D is formed from them)
+ *   d_packed   out  [B, heads, 2dk+dv_total, N], dtype: V rows [v0, v0+dv)
+ *                   are overwritten with this slice's dV; the dQ and dK
+ *                   sections are overwritten (accumulate = 0) or have this
+ *                   slice's dQ and dK added to them (accumulate != 0); other
+ *                   V rows are not touched.
+ * The page adds the calls' dQ and dK with atomics into zeroed sections; here
+ * the first call overwrites and later ones (accumulate = 1) read, add and
+ * write each element once, so no zeroing is needed and the result is
+ * bitwise reproducible.  Calls that share d_packed must be ordered (one
+ * stream): concurrent accumulating calls race.  In 16-bit storage the sum
+ * is rounded once per call.  Scratch as for psa_attn_bwd.
+ */
+int psa_attn_bwd_vslice(const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed, int B,
+                        int heads, int N, int dk, int dv_total, int v0, int dv, int accumulate, float scale,
+                        int dtype, void* stream);
+
+/*
+ * PSA merge (PsaMergeAttnRuntimeOp page: forward and backward of the op
+ * that joins the lo and hi attention outputs).  Each head's merged
+ * channels are its lo half followed by its hi half:
+ *   merged[b][h][c][n] = lo[b][h][c][n],  hi[b][h][c - half][n] for c >= half
+ * with lo, hi [B, heads, half, N] and merged [B, heads, 2*half, N] (that is
+ * [B, heads*2*half, H, W]), all in dtype.
+ * psa_merge_fwd writes merged from (o_lo, o_hi); psa_merge_bwd splits the
+ * upstream gradient d_merged into (d_lo, d_hi) by the same map.  Pure
+ * copies, no atomics, no scratch; no two of the three tensors may overlap.
+ */
+int psa_merge_fwd(const void* o_lo, const void* o_hi, void* merged, int B, int heads, int N, int half, int dtype,
+                  void* stream);
+int psa_merge_bwd(const void* d_merged, void* d_lo, void* d_hi, int B, int heads, int N, int half, int dtype,
+                  void* stream);
+
+/*
  * Backward of the 1x1 convolution that produces qkv from the block input x
  * (Conv2dBackward page, struct description, with kh = kw = 1, stride 1, no
  * padding and g = 1; no bias).  The forward is y[b][co][n] = sum_ci
@@ -149,8 +203,9 @@ int psa_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int to
                         void* stream);
 
 /* 1 if (dk, dv, dtype) has a compiled instance, else 0.  No GPU access.
- * Compiled: (dk, dv) in {(32,32), (32,64), (64,64), (64,128), (128,128)} for
- * every dtype, and (16,16) for PSA_F32. */
+ * Compiled: (dk, dv) in {(32,32), (32,64), (64,32), (64,64), (64,128),
+ * (128,128)} for every dtype, and (16,16) for PSA_F32.  (64,32) serves the
+ * halves of V at dk = dv = 64 in the V-slice calls. */
 int psa_attn_supported(int dk, int dv, int dtype);
 
 /* Message for the last non-OK status returned on the calling thread
@@ -169,9 +224,10 @@ int psa_attn_version(void);
  * 2 = backward GEMM launch (dK/dV and dQ in one grid), 3 = backward dQ
  * (used only by builds with -DPSA_BWD_SPLIT=1, where slot 2 is dK/dV),
  * 4 = psa_qkv_conv_bwd / psa_qkv_conv_cat_bwd dx, 5 = their dw (with its
- * reduction), 6 = psa_channel_cat_bwd.
+ * reduction), 6 = psa_channel_cat_bwd, 7 = psa_merge_fwd, 8 = psa_merge_bwd.
+ * The V-slice calls use slots 0-3 like psa_attn_fwd / psa_attn_bwd.
  */
-#define PSA_TIMING_SLOTS 7
+#define PSA_TIMING_SLOTS 9
 /* on != 0 enables, 0 disables.  Returns PSA_OK. */
 int psa_attn_timing_enable(int on);
 /* Waits for every recorded launch, then writes min(n, PSA_TIMING_SLOTS)

@@ -63,3 +63,24 @@ def conv1x1_cat_backward(x, w, dy, part_channels):
         out.append(flat.reshape(B, c, N))
         before += c
     return out, dw
+
+
+def psa_merge_forward(o_lo, o_hi):
+    """PsaMergeAttnRuntimeOp page (the op joining the two attention calls'
+    outputs), read as a per-head channel concatenation: merged[b][h] holds
+    o_lo[b][h]'s channels, then o_hi[b][h]'s.  [B, H, half, N] each ->
+    [B, H, 2*half, N]."""
+    B, H, half, N = np.shape(o_lo)
+    flat = channel_cat_forward([np.asarray(o_lo).reshape(-1), np.asarray(o_hi).reshape(-1)], B * H)
+    return flat.reshape(B, H, 2 * half, N)
+
+
+def psa_merge_backward(d_merged):
+    """The merge's backward: each head's channel halves of d_merged
+    [B, H, 2*half, N], as (d_lo, d_hi) [B, H, half, N]."""
+    B, H, C, N = np.shape(d_merged)
+    half = C // 2
+    flat = np.asarray(d_merged).reshape(-1)
+    lo = channel_cat_backward(flat, B * H, half * N, C * N, 0)
+    hi = channel_cat_backward(flat, B * H, half * N, C * N, half * N)
+    return lo.reshape(B, H, half, N), hi.reshape(B, H, half, N)

@@ -37,9 +37,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_supported_table(lib):
     F32, BF16, F16 = binding.PSA_F32, binding.PSA_BF16, binding.PSA_F16
-    for dk, dv in [(16, 16), (32, 32), (32, 64), (64, 64), (64, 128), (128, 128)]:
+    for dk, dv in [(16, 16), (32, 32), (32, 64), (64, 32), (64, 64), (64, 128), (128, 128)]:
         assert binding.psa_attn_supported(dk, dv, F32)
-    for dk, dv in [(32, 32), (32, 64), (64, 64), (64, 128), (128, 128)]:
+    for dk, dv in [(32, 32), (32, 64), (64, 32), (64, 64), (64, 128), (128, 128)]:
         assert binding.psa_attn_supported(dk, dv, BF16)
         assert binding.psa_attn_supported(dk, dv, F16)
     assert not binding.psa_attn_supported(128, 64, BF16)

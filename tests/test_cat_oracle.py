@@ -86,3 +86,25 @@ def test_conv_cat_single_part_is_conv():
     (dx,), dw = ca.conv1x1_cat_backward(x, w, dy, [6])
     rx, rw = co.conv1x1_backward(x, w, dy)
     assert np.array_equal(dx, rx) and np.array_equal(dw, rw)
+
+
+def test_psa_merge_round_trip_and_layout():
+    """Merged channels per head: lo then hi (numpy concatenate on the
+    channel axis of [B, H, half, N]); the backward returns the halves."""
+    rng = np.random.default_rng(16)
+    lo, hi = rng.standard_normal((2, 3, 4, 7)), rng.standard_normal((2, 3, 4, 7))
+    m = ca.psa_merge_forward(lo, hi)
+    assert np.array_equal(m, np.concatenate([lo, hi], axis=2))
+    dlo, dhi = ca.psa_merge_backward(m)
+    assert np.array_equal(dlo, lo) and np.array_equal(dhi, hi)
+    # viewed as [B, H*2*half, N] (the feature map), head h's hi half starts at channel h*8 + 4
+    assert np.array_equal(m.reshape(2, 24, 7)[:, 1 * 8 + 4:1 * 8 + 8], hi[:, 1])
+
+
+def test_psa_merge_adjoint():
+    rng = np.random.default_rng(17)
+    lo, hi, dm = (rng.standard_normal((1, 2, 3, 5)), rng.standard_normal((1, 2, 3, 5)),
+                  rng.standard_normal((1, 2, 6, 5)))
+    dlo, dhi = ca.psa_merge_backward(dm)
+    lhs = float((ca.psa_merge_forward(lo, hi) * dm).sum())
+    assert np.isclose(lhs, float((lo * dlo).sum() + (hi * dhi).sum()), rtol=1e-12)

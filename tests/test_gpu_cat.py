@@ -39,6 +39,7 @@ CAT_CASES = [
     (inputs.F16, 2, 64, 200, 135),            # offset breaks 16-byte alignment: element path
     (inputs.BF16, 4, 512 * 6400, 1024 * 6400, 512 * 6400),  # second half of a 1024-channel 80x80 map
     (inputs.BF16, 4, 512 * 6400, 1024 * 6400, 0),
+    (inputs.F32, 1, (1 << 25) + 8, (1 << 25) + 16, 8),  # just over 256 MiB moved: non-temporal path
 ]
 
 

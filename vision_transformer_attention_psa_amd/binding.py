@@ -19,11 +19,12 @@ PSA_F16 = 2
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
           4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
 
-EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_qkv_conv_bwd", "psa_qkv_conv_cat_bwd",
+EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_fwd_vslice", "psa_attn_bwd_vslice", "psa_merge_fwd",
+           "psa_merge_bwd", "psa_qkv_conv_bwd", "psa_qkv_conv_cat_bwd",
            "psa_channel_cat_bwd", "psa_attn_supported", "psa_last_error",
            "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
            "psa_attn_timing_reset")
-TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "conv_dx", "conv_dw", "cat")
+TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "conv_dx", "conv_dw", "cat", "merge_fwd", "merge_bwd")
 
 _lib = None
 
@@ -49,6 +50,14 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.psa_attn_fwd.restype = i
     lib.psa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.psa_attn_bwd.restype = i
+    lib.psa_attn_fwd_vslice.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.psa_attn_fwd_vslice.restype = i
+    lib.psa_attn_bwd_vslice.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.psa_attn_bwd_vslice.restype = i
+    lib.psa_merge_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    lib.psa_merge_fwd.restype = i
+    lib.psa_merge_bwd.argtypes = [vp, vp, vp, i, i, i, i, i, vp]
+    lib.psa_merge_bwd.restype = i
     lib.psa_qkv_conv_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.psa_qkv_conv_bwd.restype = i
     lib.psa_qkv_conv_cat_bwd.argtypes = [vp, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(i), i, vp, i, i, i,
@@ -113,6 +122,32 @@ def psa_attn_bwd(qkv: int, o: int, lse: int, dO: int, d_packed: int, B: int, hea
                  dk: int, dv: int, scale: float, dtype: int, stream: int | None) -> int:
     """Raw call with device addresses; returns the status code."""
     return load().psa_attn_bwd(qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, scale, dtype, stream)
+
+
+def psa_attn_fwd_vslice(qkv: int, o: int, lse: int, B: int, heads: int, N: int, dk: int, dv_total: int, v0: int,
+                        dv: int, scale: float, dtype: int, stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_attn_fwd_vslice(qkv, o, lse, B, heads, N, dk, dv_total, v0, dv, scale, dtype, stream)
+
+
+def psa_attn_bwd_vslice(qkv: int, o: int, lse: int, dO: int, d_packed: int, B: int, heads: int, N: int, dk: int,
+                        dv_total: int, v0: int, dv: int, accumulate: int, scale: float, dtype: int,
+                        stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_attn_bwd_vslice(qkv, o, lse, dO, d_packed, B, heads, N, dk, dv_total, v0, dv, accumulate,
+                                      scale, dtype, stream)
+
+
+def psa_merge_fwd(o_lo: int, o_hi: int, merged: int, B: int, heads: int, N: int, half: int, dtype: int,
+                  stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_merge_fwd(o_lo, o_hi, merged, B, heads, N, half, dtype, stream)
+
+
+def psa_merge_bwd(d_merged: int, d_lo: int, d_hi: int, B: int, heads: int, N: int, half: int, dtype: int,
+                  stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_merge_bwd(d_merged, d_lo, d_hi, B, heads, N, half, dtype, stream)
 
 
 # ------------------------------------------------------------ torch helpers
@@ -271,3 +306,83 @@ def channel_cat_bwd(dy, channels: int, offset: int, out=None):
                                                       C * inner, offset * inner, _dtype_code(dy),
                                                       _stream(dy)))
     return dx
+
+
+def _vslice_shape(qkv, dk: int, dv_total: int):
+    if qkv.dim() != 4 or qkv.shape[2] != 2 * dk + dv_total:
+        raise ValueError(f"qkv must be [B, heads, 2*dk+dv_total, N]; got {tuple(qkv.shape)}")
+    if not qkv.is_contiguous():
+        raise ValueError("qkv must be contiguous")
+    B, H, _, N = qkv.shape
+    return B, H, N
+
+
+def fwd_vslice(qkv, dk: int, dv_total: int, v0: int, dv: int, scale: float, out=None):
+    """Attention over V rows [v0, v0+dv): O [B, heads, dv, N] and LSE [B, heads, N]."""
+    import torch
+    B, H, N = _vslice_shape(qkv, dk, dv_total)
+    if out is None:
+        o = torch.empty((B, H, dv, N), dtype=qkv.dtype, device=qkv.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
+    else:
+        o, lse = out
+    _check("psa_attn_fwd_vslice", psa_attn_fwd_vslice(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, dk,
+                                                      dv_total, v0, dv, float(scale), _dtype_code(qkv),
+                                                      _stream(qkv)))
+    return o, lse
+
+
+def bwd_vslice(qkv, o, lse, dO, d_packed, dk: int, dv_total: int, v0: int, dv: int, scale: float,
+               accumulate: bool):
+    """Backward of one V-slice call into d_packed (in place): dV rows of the
+    slice overwritten, dQ and dK overwritten or (accumulate) added to."""
+    import torch
+    B, H, N = _vslice_shape(qkv, dk, dv_total)
+    for name, t in (("o", o), ("lse", lse), ("dO", dO), ("d_packed", d_packed)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tuple(o.shape) != (B, H, dv, N) or tuple(dO.shape) != (B, H, dv, N):
+        raise ValueError("o and dO must be [B, heads, dv, N]")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, heads, N]")
+    if tuple(d_packed.shape) != tuple(qkv.shape):
+        raise ValueError("d_packed must have qkv's shape")
+    for t in (o, dO, d_packed):
+        if t.dtype != qkv.dtype:
+            raise ValueError("o, dO and d_packed must have qkv's dtype")
+    _check("psa_attn_bwd_vslice",
+           psa_attn_bwd_vslice(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), dO.data_ptr(), d_packed.data_ptr(),
+                               B, H, N, dk, dv_total, v0, dv, 1 if accumulate else 0, float(scale),
+                               _dtype_code(qkv), _stream(qkv)))
+    return d_packed
+
+
+def merge_fwd(o_lo, o_hi, out=None):
+    """merged [B, heads, 2*half, N]: each head's lo channels, then its hi ones."""
+    import torch
+    if o_lo.dim() != 4 or o_lo.shape != o_hi.shape or o_lo.dtype != o_hi.dtype:
+        raise ValueError("o_lo and o_hi must be equal-shaped [B, heads, half, N]")
+    if not (o_lo.is_contiguous() and o_hi.is_contiguous()):
+        raise ValueError("o_lo and o_hi must be contiguous")
+    B, H, half, N = o_lo.shape
+    m = torch.empty((B, H, 2 * half, N), dtype=o_lo.dtype, device=o_lo.device) if out is None else out
+    _check("psa_merge_fwd", psa_merge_fwd(o_lo.data_ptr(), o_hi.data_ptr(), m.data_ptr(), B, H, N, half,
+                                          _dtype_code(o_lo), _stream(o_lo)))
+    return m
+
+
+def merge_bwd(d_merged, out=None):
+    """(d_lo, d_hi) [B, heads, half, N] from d_merged [B, heads, 2*half, N]."""
+    import torch
+    if d_merged.dim() != 4 or d_merged.shape[2] % 2 or not d_merged.is_contiguous():
+        raise ValueError("d_merged must be a contiguous [B, heads, 2*half, N] tensor")
+    B, H, C, N = d_merged.shape
+    half = C // 2
+    if out is None:
+        lo = torch.empty((B, H, half, N), dtype=d_merged.dtype, device=d_merged.device)
+        hi = torch.empty_like(lo)
+    else:
+        lo, hi = out
+    _check("psa_merge_bwd", psa_merge_bwd(d_merged.data_ptr(), lo.data_ptr(), hi.data_ptr(), B, H, N, half,
+                                          _dtype_code(d_merged), _stream(d_merged)))
+    return lo, hi

@@ -85,8 +85,10 @@ template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, D
 // ------------------------------------------------------- per-kernel timing
 // Slots: forward; D/LSE preprocessing; the backward GEMM launch (fused dK/dV
 // + dQ, or dK/dV alone when split); dQ when split; the 1x1-conv backward's
-// dx GEMM; its dw GEMM (with the split reduction); the channel-cat slice copy.
-enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5, K_CAT = 6 };
+// dx GEMM; its dw GEMM (with the split reduction); the channel-cat slice copy;
+// the PSA merge forward and backward copies.
+enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5, K_CAT = 6, K_MERGE_FWD = 7,
+       K_MERGE_BWD = 8 };
 
 struct Timing {
   std::mutex mu;
@@ -184,7 +186,7 @@ int check_launch(const char* what) {
 template <typename T> constexpr bool vec_ok(int N) { return N % (16 / (int)sizeof(T)) == 0; }
 
 template <typename T, int DK, int DV, class C>
-int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hipStream_t st) {
+int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, psa::PackView pv, hipStream_t st) {
   constexpr int BM = C::FWD_NW * 16 * C::FWD_QB;
   const int nqt = (N + BM - 1) / BM;
   const long long grid = (long long)BH * nqt;
@@ -194,16 +196,16 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, hi
   TimedLaunch tl(K_FWD, st);
   if (vec_ok<T>(N))
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true>), g, b, 0, st,
-                       (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c);
+                       (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   else
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, false>), g, b, 0, st,
-                       (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c);
+                       (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   return check_launch("psa_attn_fwd launch");
 }
 
 template <typename T, int DK, int DV, class C>
 int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, void* dpk, int BH, int N,
-            float scale, hipStream_t st) {
+            float scale, psa::PackView pv, hipStream_t st) {
   const float c = scale * psa::kLog2e;
   const long long total = (long long)BH * N;
   constexpr int BNK = 4 * 16 * C::DKDV_KB;  // keys per dK/dV workgroup
@@ -230,20 +232,20 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     TimedLaunch tl(K_MAIN, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, true>), dim3(nkb), dim3(256),
-                         0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale);
+                         0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
     else
       hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, false>), dim3(nkb),
-                         dim3(256), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale);
+                         dim3(256), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
     rc = check_launch("psa_attn_bwd dK/dV launch");
   }
   if (rc == PSA_OK) {
     TimedLaunch tl(K_DQ, st);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, true>), dim3(nqb), dim3(256), 0, st,
-                         (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale);
+                         (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale, pv);
     else
       hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, false>), dim3(nqb), dim3(256), 0,
-                         st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale);
+                         st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale, pv);
     rc = check_launch("psa_attn_bwd dQ launch");
   }
 #else
@@ -253,11 +255,11 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     if (vec_ok<T>(N))
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, true>), grid, block, 0,
-          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale);
+          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     else
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, false>), grid, block, 0,
-          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale);
+          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     rc = check_launch("psa_attn_bwd launch");
   }
 #endif
@@ -317,23 +319,60 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
   return rc;
 }
 
+// n_parts (1 or 2) parts of n_outer runs of `run` elements; see
+// psa_rows_copy_kernel.
+template <typename T>
+int run_rows_copy(const char* fn, int slot, const psa::RowCopy<T>& rc, int n_parts, long long run, int n_outer,
+                  hipStream_t st) {
+  constexpr int V = 16 / (int)sizeof(T);
+  bool vec = run % V == 0;
+  for (int p = 0; p < n_parts; ++p)
+    vec = vec && rc.src_row[p] % V == 0 && rc.dst_row[p] % V == 0 && ((uintptr_t)rc.src[p] & 15u) == 0 &&
+          ((uintptr_t)rc.dst[p] & 15u) == 0;
+  const long long per_launch = 256LL * psa::kCatUnroll;
+  const long long per_row = ((vec ? run / V : run) + per_launch - 1) / per_launch;
+  const long long grid = per_row * n_outer * n_parts;
+  if (grid > INT32_MAX) return fail(PSA_ERR_SHAPE, std::string(fn) + ": grid too large");
+  // non-temporal accesses once the copy (read + write) outgrows the 256 MiB
+  // last-level cache
+  const bool nt = vec && 2.0 * n_parts * n_outer * run * sizeof(T) > 256.0 * (1 << 20);
+  TimedLaunch tl(slot, st);
+  const dim3 g((unsigned)grid), blk(256);
+  if (nt)
+    hipLaunchKernelGGL((psa::psa_rows_copy_kernel<T, true, true>), g, blk, 0, st, rc, run, (int)per_row, n_outer);
+  else if (vec)
+    hipLaunchKernelGGL((psa::psa_rows_copy_kernel<T, true, false>), g, blk, 0, st, rc, run, (int)per_row, n_outer);
+  else
+    hipLaunchKernelGGL((psa::psa_rows_copy_kernel<T, false, false>), g, blk, 0, st, rc, run, (int)per_row, n_outer);
+  return check_launch((std::string(fn) + " launch").c_str());
+}
+
 template <typename T>
 int run_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int total, int offset, hipStream_t st) {
-  constexpr int V = 16 / (int)sizeof(T);
-  const bool vec = chunk % V == 0 && total % V == 0 && offset % V == 0;
-  const long long per_vec = 256LL * psa::kCatUnroll;
-  const long long units = vec ? chunk / V : chunk;
-  const long long per_row = (units + per_vec - 1) / per_vec;
-  const long long grid = per_row * n_outer;
-  if (grid > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_channel_cat_bwd: grid too large");
-  TimedLaunch tl(K_CAT, st);
-  if (vec)
-    hipLaunchKernelGGL((psa::psa_channel_cat_bwd_kernel<T, true>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const T*)dy, (T*)dx, (long long)chunk, (long long)total, (long long)offset, (int)per_row);
-  else
-    hipLaunchKernelGGL((psa::psa_channel_cat_bwd_kernel<T, false>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const T*)dy, (T*)dx, (long long)chunk, (long long)total, (long long)offset, (int)per_row);
-  return check_launch("psa_channel_cat_bwd launch");
+  psa::RowCopy<T> rc{};
+  rc.src[0] = rc.src[1] = (const T*)dy + offset;
+  rc.dst[0] = rc.dst[1] = (T*)dx;
+  rc.src_row[0] = rc.src_row[1] = total;
+  rc.dst_row[0] = rc.dst_row[1] = chunk;
+  return run_rows_copy<T>("psa_channel_cat_bwd", K_CAT, rc, 1, chunk, n_outer, st);
+}
+
+// merged [BH, 2*half, N] <-> (lo, hi) [BH, half, N]
+template <typename T>
+int run_merge(bool forward, const void* a, const void* b, const void* m, int BH, int half, int N, hipStream_t st) {
+  const long long run = (long long)half * N;
+  psa::RowCopy<T> rc{};
+  const T* lo = (const T*)a;
+  const T* hi = (const T*)b;
+  T* mg = (T*)m;
+  if (forward) {
+    rc.src[0] = lo, rc.src[1] = hi, rc.dst[0] = mg, rc.dst[1] = mg + run;
+    rc.src_row[0] = rc.src_row[1] = run, rc.dst_row[0] = rc.dst_row[1] = 2 * run;
+    return run_rows_copy<T>("psa_merge_fwd", K_MERGE_FWD, rc, 2, run, BH, st);
+  }
+  rc.src[0] = mg, rc.src[1] = mg + run, rc.dst[0] = (T*)lo, rc.dst[1] = (T*)hi;
+  rc.src_row[0] = rc.src_row[1] = 2 * run, rc.dst_row[0] = rc.dst_row[1] = run;
+  return run_rows_copy<T>("psa_merge_bwd", K_MERGE_BWD, rc, 2, run, BH, st);
 }
 
 // ------------------------------------------------------------ instance table
@@ -341,16 +380,19 @@ int run_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int to
   X(PSA_F32, float, 16, 16)     \
   X(PSA_F32, float, 32, 32)     \
   X(PSA_F32, float, 32, 64)     \
+  X(PSA_F32, float, 64, 32)     \
   X(PSA_F32, float, 64, 64)     \
   X(PSA_F32, float, 64, 128)    \
   X(PSA_F32, float, 128, 128)   \
   X(PSA_BF16, psa::bf16, 32, 32) \
   X(PSA_BF16, psa::bf16, 32, 64) \
+  X(PSA_BF16, psa::bf16, 64, 32) \
   X(PSA_BF16, psa::bf16, 64, 64) \
   X(PSA_BF16, psa::bf16, 64, 128) \
   X(PSA_BF16, psa::bf16, 128, 128) \
   X(PSA_F16, psa::f16, 32, 32)   \
   X(PSA_F16, psa::f16, 32, 64)   \
+  X(PSA_F16, psa::f16, 64, 32)   \
   X(PSA_F16, psa::f16, 64, 64)   \
   X(PSA_F16, psa::f16, 64, 128)  \
   X(PSA_F16, psa::f16, 128, 128)
@@ -408,6 +450,77 @@ int check_device(const char* fn) {
   }
   if (known[dev] != 1) return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": device is not gfx950");
   return PSA_OK;
+}
+
+// One attention call over V rows [v0, v0 + dv) of a packed buffer with
+// 2dk + dv_total channels per slice (v0 = 0, dv = dv_total: all of V).
+int check_vslice(const char* fn, int dv_total, int v0, int dv) {
+  if (dv_total < 1 || v0 < 0 || (long long)v0 + dv > dv_total)
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": need 0 <= v0 and v0 + dv <= dv_total");
+  return PSA_OK;
+}
+
+int attn_fwd_impl(const char* fn, const void* qkv, void* o, float* lse, int B, int heads, int N, int dk,
+                  int dv_total, int v0, int dv, float scale, int dtype, void* stream) {
+  g_err.clear();
+  if (!qkv || !o || !lse) return fail(PSA_ERR_NULL, std::string(fn) + ": qkv, o and lse must be non-NULL");
+  int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
+  if (rc != PSA_OK) return rc;
+  if ((rc = check_vslice(fn, dv_total, v0, dv)) != PSA_OK) return rc;
+  if ((__int128)B * heads * (2 * (__int128)dk + dv_total) * N > ((__int128)1 << 46))
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": problem too large");
+  if (misaligned(qkv) || misaligned(o) || misaligned(lse))
+    return fail(PSA_ERR_ALIGN, std::string(fn) + ": base pointers must be 16-byte aligned");
+  const size_t e = elem_size(dtype), BH = (size_t)B * heads;
+  const Range rq{(uintptr_t)qkv, (uintptr_t)qkv + BH * (2 * dk + dv_total) * N * e};
+  const Range ro{(uintptr_t)o, (uintptr_t)o + BH * dv * N * e};
+  const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
+  if (overlap(ro, rq) || overlap(rl, rq) || overlap(ro, rl))
+    return fail(PSA_ERR_ALIAS, std::string(fn) + ": o, lse and qkv must not overlap");
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, 0};
+#define X(DT, T, K, V)                                                                                   \
+  if (dtype == DT && dk == K && dv == V)                                                                 \
+    return N <= PSA_SMALL_N_MAX ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st) \
+                                : run_fwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st);
+  PSA_INSTANCES(X)
+#undef X
+  return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": no instance");
+}
+
+int attn_bwd_impl(const char* fn, const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed,
+                  int B, int heads, int N, int dk, int dv_total, int v0, int dv, bool accum, float scale, int dtype,
+                  void* stream) {
+  g_err.clear();
+  if (!qkv || !o || !lse || !dO || !d_packed)
+    return fail(PSA_ERR_NULL, std::string(fn) + ": qkv, o, lse, dO and d_packed must be non-NULL");
+  int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
+  if (rc != PSA_OK) return rc;
+  if ((rc = check_vslice(fn, dv_total, v0, dv)) != PSA_OK) return rc;
+  if ((__int128)B * heads * (2 * (__int128)dk + dv_total) * N > ((__int128)1 << 46))
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": problem too large");
+  if (misaligned(qkv) || misaligned(o) || misaligned(lse) || misaligned(dO) || misaligned(d_packed))
+    return fail(PSA_ERR_ALIGN, std::string(fn) + ": base pointers must be 16-byte aligned");
+  const size_t e = elem_size(dtype), BH = (size_t)B * heads;
+  const Range rd{(uintptr_t)d_packed, (uintptr_t)d_packed + BH * (2 * dk + dv_total) * N * e};
+  const Range rq{(uintptr_t)qkv, (uintptr_t)qkv + BH * (2 * dk + dv_total) * N * e};
+  const Range ro{(uintptr_t)o, (uintptr_t)o + BH * dv * N * e};
+  const Range rg{(uintptr_t)dO, (uintptr_t)dO + BH * dv * N * e};
+  const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
+  if (overlap(rd, rq) || overlap(rd, ro) || overlap(rd, rg) || overlap(rd, rl))
+    return fail(PSA_ERR_ALIAS, std::string(fn) + ": d_packed must not overlap any input");
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, accum ? 1 : 0};
+#define X(DT, T, K, V)                                                                                        \
+  if (dtype == DT && dk == K && dv == V)                                                                      \
+    return N <= PSA_SMALL_N_MAX                                                                               \
+               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st) \
+               : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st);
+  PSA_INSTANCES(X)
+#undef X
+  return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": no instance");
 }
 
 int conv_bwd_impl(const char* fn, const void* x, const void* w, const void* dy, void* const* dx_parts,
@@ -528,58 +641,25 @@ int psa_attn_timing_reset(void) {
 
 int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N, int dk, int dv, float scale,
                  int dtype, void* stream) {
-  g_err.clear();
-  const char* fn = "psa_attn_fwd";
-  if (!qkv || !o || !lse) return fail(PSA_ERR_NULL, "psa_attn_fwd: qkv, o and lse must be non-NULL");
-  int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
-  if (rc != PSA_OK) return rc;
-  if (misaligned(qkv) || misaligned(o) || misaligned(lse))
-    return fail(PSA_ERR_ALIGN, "psa_attn_fwd: base pointers must be 16-byte aligned");
-  const size_t e = elem_size(dtype), BH = (size_t)B * heads;
-  const Range rq{(uintptr_t)qkv, (uintptr_t)qkv + BH * (2 * dk + dv) * N * e};
-  const Range ro{(uintptr_t)o, (uintptr_t)o + BH * dv * N * e};
-  const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
-  if (overlap(ro, rq) || overlap(rl, rq) || overlap(ro, rl))
-    return fail(PSA_ERR_ALIAS, "psa_attn_fwd: o, lse and qkv must not overlap");
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
-  hipStream_t st = (hipStream_t)stream;
-#define X(DT, T, K, V)                                                                     \
-  if (dtype == DT && dk == K && dv == V)                                                   \
-    return N <= PSA_SMALL_N_MAX ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, (int)BH, N, scale, st) \
-                                : run_fwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, (int)BH, N, scale, st);
-  PSA_INSTANCES(X)
-#undef X
-  return fail(PSA_ERR_UNSUPPORTED, "psa_attn_fwd: no instance");
+  return attn_fwd_impl("psa_attn_fwd", qkv, o, lse, B, heads, N, dk, dv, 0, dv, scale, dtype, stream);
 }
 
 int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed, int B,
                  int heads, int N, int dk, int dv, float scale, int dtype, void* stream) {
-  g_err.clear();
-  const char* fn = "psa_attn_bwd";
-  if (!qkv || !o || !lse || !dO || !d_packed)
-    return fail(PSA_ERR_NULL, "psa_attn_bwd: qkv, o, lse, dO and d_packed must be non-NULL");
-  int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
-  if (rc != PSA_OK) return rc;
-  if (misaligned(qkv) || misaligned(o) || misaligned(lse) || misaligned(dO) || misaligned(d_packed))
-    return fail(PSA_ERR_ALIGN, "psa_attn_bwd: base pointers must be 16-byte aligned");
-  const size_t e = elem_size(dtype), BH = (size_t)B * heads;
-  const Range rd{(uintptr_t)d_packed, (uintptr_t)d_packed + BH * (2 * dk + dv) * N * e};
-  const Range rq{(uintptr_t)qkv, (uintptr_t)qkv + BH * (2 * dk + dv) * N * e};
-  const Range ro{(uintptr_t)o, (uintptr_t)o + BH * dv * N * e};
-  const Range rg{(uintptr_t)dO, (uintptr_t)dO + BH * dv * N * e};
-  const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
-  if (overlap(rd, rq) || overlap(rd, ro) || overlap(rd, rg) || overlap(rd, rl))
-    return fail(PSA_ERR_ALIAS, "psa_attn_bwd: d_packed must not overlap any input");
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
-  hipStream_t st = (hipStream_t)stream;
-#define X(DT, T, K, V)                                                                              \
-  if (dtype == DT && dk == K && dv == V)                                                            \
-    return N <= PSA_SMALL_N_MAX                                                                     \
-               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st) \
-               : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, st);
-  PSA_INSTANCES(X)
-#undef X
-  return fail(PSA_ERR_UNSUPPORTED, "psa_attn_bwd: no instance");
+  return attn_bwd_impl("psa_attn_bwd", qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, 0, dv, 0, scale, dtype,
+                       stream);
+}
+
+int psa_attn_fwd_vslice(const void* qkv, void* o, float* lse, int B, int heads, int N, int dk, int dv_total, int v0,
+                        int dv, float scale, int dtype, void* stream) {
+  return attn_fwd_impl("psa_attn_fwd_vslice", qkv, o, lse, B, heads, N, dk, dv_total, v0, dv, scale, dtype, stream);
+}
+
+int psa_attn_bwd_vslice(const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed, int B,
+                        int heads, int N, int dk, int dv_total, int v0, int dv, int accumulate, float scale,
+                        int dtype, void* stream) {
+  return attn_bwd_impl("psa_attn_bwd_vslice", qkv, o, lse, dO, d_packed, B, heads, N, dk, dv_total, v0, dv,
+                       accumulate != 0, scale, dtype, stream);
 }
 
 int psa_qkv_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin, int cout,
@@ -617,6 +697,41 @@ int psa_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int to
   if (dtype == PSA_F32) return run_channel_cat_bwd<float>(dy, dx, n_outer, chunk, total, offset, st);
   if (dtype == PSA_BF16) return run_channel_cat_bwd<psa::bf16>(dy, dx, n_outer, chunk, total, offset, st);
   return run_channel_cat_bwd<psa::f16>(dy, dx, n_outer, chunk, total, offset, st);
+}
+
+static int merge_impl(bool forward, const char* fn, const void* lo, const void* hi, const void* merged, int B,
+                      int heads, int N, int half, int dtype, void* stream) {
+  g_err.clear();
+  if (!lo || !hi || !merged) return fail(PSA_ERR_NULL, std::string(fn) + ": all pointers must be non-NULL");
+  if (dtype != PSA_F32 && dtype != PSA_BF16 && dtype != PSA_F16)
+    return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": unknown dtype");
+  if (B < 1 || heads < 1 || N < 1 || half < 1)
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": B, heads, N, half must be >= 1");
+  if ((__int128)B * heads > INT32_MAX || (__int128)B * heads * 2 * half * N > ((__int128)1 << 46))
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": problem too large");
+  if (misaligned(lo) || misaligned(hi) || misaligned(merged))
+    return fail(PSA_ERR_ALIGN, std::string(fn) + ": base pointers must be 16-byte aligned");
+  const size_t e = elem_size(dtype), BH = (size_t)B * heads, part = BH * half * N * e;
+  const Range rlo{(uintptr_t)lo, (uintptr_t)lo + part}, rhi{(uintptr_t)hi, (uintptr_t)hi + part};
+  const Range rm{(uintptr_t)merged, (uintptr_t)merged + 2 * part};
+  if (overlap(rlo, rhi) || overlap(rlo, rm) || overlap(rhi, rm))
+    return fail(PSA_ERR_ALIAS, std::string(fn) + ": lo, hi and merged must not overlap");
+  int rc;
+  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == PSA_F32) return run_merge<float>(forward, lo, hi, merged, (int)BH, half, N, st);
+  if (dtype == PSA_BF16) return run_merge<psa::bf16>(forward, lo, hi, merged, (int)BH, half, N, st);
+  return run_merge<psa::f16>(forward, lo, hi, merged, (int)BH, half, N, st);
+}
+
+int psa_merge_fwd(const void* o_lo, const void* o_hi, void* merged, int B, int heads, int N, int half, int dtype,
+                  void* stream) {
+  return merge_impl(true, "psa_merge_fwd", o_lo, o_hi, merged, B, heads, N, half, dtype, stream);
+}
+
+int psa_merge_bwd(const void* d_merged, void* d_lo, void* d_hi, int B, int heads, int N, int half, int dtype,
+                  void* stream) {
+  return merge_impl(false, "psa_merge_bwd", d_lo, d_hi, d_merged, B, heads, N, half, dtype, stream);
 }
 
 }  // extern "C"

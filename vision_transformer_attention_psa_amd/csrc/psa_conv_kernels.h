@@ -231,37 +231,68 @@ __global__ __launch_bounds__(256) void psa_conv_dw_reduce_kernel(const float* __
   dw[i] = from_f32<T>(v);
 }
 
-// ------------------------------------------------------- channel-cat backward
-// ChannelCatBackward page, struct description: one input's gradient is its
-// slice of the concatenated upstream gradient.  Per outer index n (the
-// batch), dx holds chunk contiguous elements and dy holds total, of which
-// the input's are [off, off + chunk):
-//   dx[n * chunk + e] = dy[n * total + off + e],  e < chunk.
-// (For a channel concatenation of [C_k, H, W] tensors, chunk = C_k*H*W and
-// off = (channels before input k)*H*W.)  Workgroup blk copies segment
-// blk % per_row (256 * kCatUnroll vectors) of run n = blk / per_row, in
-// 16-byte vectors when chunk, total and off are multiples of 16 bytes,
-// else element by element.
-constexpr int kCatUnroll = 4;  // vectors (or elements) per thread
+// ------------------------------------------------------------ row copies
+// Channel concatenation and its backward move whole channel ranges, which
+// in a [n][channels][tokens] tensor are contiguous runs: for every outer
+// index n (batch, or batch x head) one run of `run` elements per part,
+//   dst_p[n * dst_row_p + e] = src_p[n * src_row_p + e],   e < run,
+// with any channel offset folded into the part's base pointers.
+//   channel-cat backward (ChannelCatBackward page, struct description):
+//     one part, src = dy + offset, src_row = total, dst_row = chunk;
+//   PSA merge forward / backward (PsaMergeAttnRuntimeOp page): two parts,
+//     the lo and hi halves of each head's channels.
+// Workgroup blk: part p = blk / (per_row * n_outer), then run n and segment
+// (256 * kCatUnroll vectors) of it; 16-byte vectors when every row length
+// and base offset allows, else single elements.
+#ifndef PSA_CAT_UNROLL
+#define PSA_CAT_UNROLL 2
+#endif
+constexpr int kCatUnroll = PSA_CAT_UNROLL;  // vectors (or elements) per thread
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void psa_channel_cat_bwd_kernel(const T* __restrict__ dy, T* __restrict__ dx,
-                                                                  long long run, long long dy_row, long long off,
-                                                                  int per_row) {
+template <typename T>
+struct RowCopy {
+  const T* src[2];
+  T* dst[2];
+  long long src_row[2], dst_row[2];
+};
+
+// NT: non-temporal loads and stores, for copies too large to stay in the
+// last-level cache, where they measured faster; smaller copies measured
+// faster with ordinary accesses.
+template <typename T, bool VEC, bool NT>
+__global__ __launch_bounds__(256) void psa_rows_copy_kernel(const RowCopy<T> rc, long long run, int per_row,
+                                                            int n_outer) {
   constexpr int V = VEC ? 16 / (int)sizeof(T) : 1;
   typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
   using Vec = typename std::conditional<VEC, u32x4v, T>::type;
-  const int blk = block_id(), n = blk / per_row, seg = blk - n * per_row;
-  const Vec* src = (const Vec*)(dy + (size_t)n * dy_row + off);
-  Vec* dst = (Vec*)(dx + (size_t)n * run);
+  const int per_part = per_row * n_outer;
+  const int blk0 = block_id();
+  const bool p1 = blk0 >= per_part;  // uniform: selects, no indexing into the argument struct
+  const int blk = p1 ? blk0 - per_part : blk0;
+  const int n = blk / per_row, seg = blk - n * per_row;
+  const T* sbase = p1 ? rc.src[1] : rc.src[0];
+  T* dbase = p1 ? rc.dst[1] : rc.dst[0];
+  const long long srow = p1 ? rc.src_row[1] : rc.src_row[0], drow = p1 ? rc.dst_row[1] : rc.dst_row[0];
+  const Vec* src = (const Vec*)(sbase + (size_t)n * srow);
+  Vec* dst = (Vec*)(dbase + (size_t)n * drow);
   const long long nv = run / V, k0 = (long long)seg * 256 * kCatUnroll + thread_id();
   Vec r[kCatUnroll];
 #pragma unroll
   for (int u = 0; u < kCatUnroll; ++u)
-    if (k0 + u * 256 < nv) r[u] = src[k0 + u * 256];
+    if (k0 + u * 256 < nv) {
+      if constexpr (NT)
+        r[u] = __builtin_nontemporal_load(src + k0 + u * 256);
+      else
+        r[u] = src[k0 + u * 256];
+    }
 #pragma unroll
   for (int u = 0; u < kCatUnroll; ++u)
-    if (k0 + u * 256 < nv) dst[k0 + u * 256] = r[u];
+    if (k0 + u * 256 < nv) {
+      if constexpr (NT)
+        __builtin_nontemporal_store(r[u], dst + k0 + u * 256);
+      else
+        dst[k0 + u * 256] = r[u];
+    }
 }
 
 }  // namespace psa

@@ -30,6 +30,8 @@
 // queries (dK/dV); their rows are permuted within each 32-token chunk (see
 // psa_common.h) so that P and dS become the next MFMA operand in place.
 #pragma once
+#include <type_traits>
+
 #include "psa_common.h"
 
 namespace psa {
@@ -52,16 +54,27 @@ template <int D> struct Chunks {
 template <typename T, typename S>
 __device__ __forceinline__ T* tm_of(T* base, const S&) { return base + S::NAT_ELEMS; }
 
+// Where one call's channels sit in the packed buffers.  qkv and d_packed
+// hold cs channels per slice: Q at [0, dk), K at [dk, 2dk), and this call's
+// V rows from channel voff (cs = 2dk + dv, voff = 2dk for a call over all
+// of V; a call over a slice of V has cs = 2dk + dv_total and DV = its own
+// width).  accum != 0: the backward adds its dQ and dK to what d_packed
+// holds instead of overwriting them (dV rows are always overwritten).
+struct PackView {
+  int cs, voff, accum;
+};
+
 // =================================================================== forward
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
                                                          float* __restrict__ lse, int N, int n_qtiles,
-                                                         int n_blocks, float c /* scale * log2(e) */) {
+                                                         int n_blocks, float c /* scale * log2(e) */,
+                                                         const PackView pv) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
   // K|V tile: K rows token-major (bf16) for S^T, V rows channel-major for PV.
-  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK + DV, DK, DK, DK + DV>;
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, DK, DK, DK + DV>;
   using SQ = Stager<T, DK, BM, NT, VECOK, DK, DK, 0, 0>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   constexpr int QE = SQ::NAT_ELEMS + SQ::TM_ELEMS;
@@ -72,8 +85,9 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int blk = xcd_remap(block_id(), n_blocks);
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
-  const T* Qg = qkv + (size_t)bh * (2 * DK + DV) * N;
+  const T* Qg = qkv + (size_t)bh * pv.cs * N;
   const T* KVg = Qg + (size_t)DK * N;
+  const T* Vg = Qg + (size_t)pv.voff * N;
 
   // Stationary queries: B operands of S^T = K Q^T (lane = query column).
   Frag<T> qf[QB][KC];
@@ -91,7 +105,7 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
   }
 
   SKV st;
-  st.load(KVg, KVg, N, 0, tid);
+  st.load(KVg, Vg, N, 0, tid);
   st.store(smem, tm_of(smem, st), tid);
   __syncthreads();
 
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
     T* nat = smem + (kt & 1) * BUF;
     const T* tm = tm_of(nat, st);
     const T* Vt = nat + (VROW + 0) * SKV::LDN;
-    if (kt + 1 < nkt) st.load(KVg, KVg, N, (kt + 1) * BN, tid);
+    if (kt + 1 < nkt) st.load(KVg, Vg, N, (kt + 1) * BN, tid);
     const int j0 = kt * BN;
 
 #pragma unroll
@@ -236,7 +250,7 @@ struct DkdvShape {
   static constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
   // Q|dO tile: both layouts of every row.  K|V stationary tile: token-major.
   using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, DK + DV, 0, DK + DV>;
-  using SKV = Stager<T, DK + DV, BNK, NT, true, DK + DV, DK + DV, 0, 0>;
+  using SKV = Stager<T, DK + DV, BNK, NT, true, DK, DK + DV, 0, 0>;
   static constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 4 * BMQ * (int)sizeof(float);
   static_assert(2 * TILE * sizeof(T) % 16 == 0, "statistics must be 16-byte aligned");
@@ -248,14 +262,14 @@ template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
 __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T* __restrict__ dO,
                                               const float* __restrict__ nlg, const float* __restrict__ ndg,
                                               T* __restrict__ dpk, int N,
-                                              int n_ktiles, float c, float scale, int blk,
-                                              unsigned char* smem_raw) {
+                                              int n_ktiles, float c, float scale, const PackView pv,
+                                              int blk, unsigned char* smem_raw) {
   using Shape = DkdvShape<T, DK, DV, KB, NW, BMQ>;
   constexpr int KW = Shape::KW, BNK = Shape::BNK, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BMQ % 32 == 0, "query tile must be a multiple of 32");
   using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, DK + DV, 0, DK + DV>;
-  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK + DV, DK + DV, 0, 0>;
+  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK, DK + DV, 0, 0>;
   constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   T* smem = (T*)smem_raw;
   float* snl = (float*)(smem_raw + 2 * TILE * sizeof(T));  // [2][BMQ], then snd [2][BMQ]
@@ -263,9 +277,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int bh = blk / n_ktiles, j0 = (blk - bh * n_ktiles) * BNK;
-  const size_t C = 2 * DK + DV;
+  const size_t C = pv.cs;
   const T* Qg = qkv + (size_t)bh * C * N;
   const T* KVg = Qg + (size_t)DK * N;
+  const T* Vg = Qg + (size_t)pv.voff * N;
   const T* dOg = dO + (size_t)bh * DV * N;
   const float* nlq = nlg + (size_t)bh * N;
   const float* ndq = ndg + (size_t)bh * N;
@@ -274,7 +289,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   Frag<T> kf[KB][KC], vf[KB][CC];
   {
     SKV sk;
-    sk.load(KVg, KVg, N, j0, tid);
+    sk.load(KVg, Vg, N, j0, tid);
     sk.store(smem, tm_of(smem, sk), tid);
     __syncthreads();
     const T* tm = tm_of(smem, sk);
@@ -394,21 +409,30 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
     __syncthreads();
   }
 
+  auto epilogue = [&](auto accum) {
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const int j = j0 + w * KW + 16 * kb + t;
-    if (j < N) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const int j = j0 + w * KW + 16 * kb + t;
+      if (j < N) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int db = 0; db < DK / 16; ++db)
-          dpk[((size_t)bh * C + DK + 16 * db + 4 * g + r) * N + j] = from_f32<T>(dkacc[db][kb][r] * scale);
+          for (int db = 0; db < DK / 16; ++db) {
+            T* p = dpk + ((size_t)bh * C + DK + 16 * db + 4 * g + r) * N + j;
+            const float v = dkacc[db][kb][r] * scale;
+            *p = from_f32<T>(decltype(accum)::value ? to_f32(*p) + v : v);
+          }
 #pragma unroll
-        for (int cb = 0; cb < DV / 16; ++cb)
-          dpk[((size_t)bh * C + 2 * DK + 16 * cb + 4 * g + r) * N + j] = from_f32<T>(dvacc[cb][kb][r]);
+          for (int cb = 0; cb < DV / 16; ++cb)
+            dpk[((size_t)bh * C + pv.voff + 16 * cb + 4 * g + r) * N + j] = from_f32<T>(dvacc[cb][kb][r]);
+        }
       }
     }
-  }
+  };
+  if (pv.accum)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 // =============================================================== backward dQ
@@ -418,7 +442,7 @@ template <typename T, int DK, int DV, int QB, int NW, int BN>
 struct DqShape {
   static constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T).
-  using SKV = Stager<T, DK + DV, BN, NT, true, DK + DV, DK + DV, 0, DK>;
+  using SKV = Stager<T, DK + DV, BN, NT, true, DK, DK + DV, 0, DK>;
   // Stationary Q|dO tile, token-major.
   using SQG = Stager<T, DK + DV, BM, NT, true, DK, DK + DV, 0, 0>;
   static constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
@@ -429,22 +453,23 @@ struct DqShape {
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
 __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* __restrict__ dO,
                                             const float* __restrict__ nlg, const float* __restrict__ ndg,
-                                            T* __restrict__ dpk, int N,
-                                            int n_qtiles, float c, float scale, int blk, unsigned char* smem_raw) {
+                                            T* __restrict__ dpk, int N, int n_qtiles, float c, float scale,
+                                            const PackView pv, int blk, unsigned char* smem_raw) {
   using Shape = DqShape<T, DK, DV, QB, NW, BN>;
   constexpr int QW = Shape::QW, BM = Shape::BM, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
-  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK + DV, DK + DV, 0, DK>;
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, DK + DV, 0, DK>;
   using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, DK + DV, 0, 0>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   T* smem = (T*)smem_raw;
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
-  const size_t C = 2 * DK + DV;
+  const size_t C = pv.cs;
   const T* Qg = qkv + (size_t)bh * C * N;
   const T* KVg = Qg + (size_t)DK * N;
+  const T* Vg = Qg + (size_t)pv.voff * N;
   const T* dOg = dO + (size_t)bh * DV * N;
 
   // Stationary queries: B operands of S^T = K Q^T and dP^T = V dO^T.  Their
@@ -479,7 +504,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
     for (int db = 0; db < DK / 16; ++db) dqacc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   SKV sk;
-  sk.load(KVg, KVg, N, 0, tid);
+  sk.load(KVg, Vg, N, 0, tid);
   sk.store(smem, tm_of(smem, sk), tid);
   __syncthreads();
 
@@ -487,7 +512,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   for (int kt = 0; kt < nkt; ++kt) {
     const T* nat = smem + (kt & 1) * BUF;  // K channel-major (fp32: K then V)
     const T* tm = tm_of(nat, sk);          // K then V channels, token-major
-    if (kt + 1 < nkt) sk.load(KVg, KVg, N, (kt + 1) * BN, tid);
+    if (kt + 1 < nkt) sk.load(KVg, Vg, N, (kt + 1) * BN, tid);
 
 #pragma unroll
     for (int c2 = 0; c2 < BN / 32; ++c2) {
@@ -542,35 +567,44 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
     __syncthreads();
   }
 
+  auto epilogue = [&](auto accum) {
 #pragma unroll
-  for (int nb = 0; nb < QB; ++nb) {
-    const int i = i0 + w * QW + 16 * nb + t;
-    if (i < N) {
+    for (int nb = 0; nb < QB; ++nb) {
+      const int i = i0 + w * QW + 16 * nb + t;
+      if (i < N) {
 #pragma unroll
-      for (int db = 0; db < DK / 16; ++db)
+        for (int db = 0; db < DK / 16; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dpk[((size_t)bh * C + 16 * db + 4 * g + r) * N + i] = from_f32<T>(dqacc[db][nb][r] * scale);
+          for (int r = 0; r < 4; ++r) {
+            T* p = dpk + ((size_t)bh * C + 16 * db + 4 * g + r) * N + i;
+            const float v = dqacc[db][nb][r] * scale;
+            *p = from_f32<T>(decltype(accum)::value ? to_f32(*p) + v : v);
+          }
+      }
     }
-  }
+  };
+  if (pv.accum)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 
 // ========================================================= backward kernels
 template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dkdv_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
-    T* __restrict__ dpk, int N, int n_ktiles, int n_blocks, float c, float scale) {
+    T* __restrict__ dpk, int N, int n_ktiles, int n_blocks, float c, float scale, const PackView pv) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM];
-  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale,
+  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
                                                xcd_remap(block_id(), n_blocks), smem);
 }
 
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
-    T* __restrict__ dpk, int N, int n_qtiles, int n_blocks, float c, float scale) {
+    T* __restrict__ dpk, int N, int n_qtiles, int n_blocks, float c, float scale, const PackView pv) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[DqShape<T, DK, DV, QB, NW, BN>::SMEM];
-  bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale,
+  bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale, pv,
                                              xcd_remap(block_id(), n_blocks), smem);
 }
 
@@ -582,15 +616,16 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
 template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, bool VECOK>
 __global__ __launch_bounds__(256) PSA_OCCUPANCY void psa_bwd_fused_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
-    T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale) {
+    T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale,
+    const PackView pv) {
   constexpr int S1 = DkdvShape<T, DK, DV, KB, 4, BMQ>::SMEM, S2 = DqShape<T, DK, DV, QB, 4, BN>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S1 > S2 ? S1 : S2];
   const int b = block_id();
   if (b < n_kblocks)
-    bwd_dkdv_body<T, DK, DV, KB, 4, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale,
+    bwd_dkdv_body<T, DK, DV, KB, 4, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
                                                 xcd_remap(b, n_kblocks), smem);
   else
-    bwd_dq_body<T, DK, DV, QB, 4, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale,
+    bwd_dq_body<T, DK, DV, QB, 4, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale, pv,
                                              xcd_remap(b - n_kblocks, n_qblocks), smem);
 }
 
