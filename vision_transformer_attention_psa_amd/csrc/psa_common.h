@@ -263,14 +263,11 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = e >> 1;
-          unsigned w0, w1;
-          if (e & 1) {
-            w0 = (r[u][0][d] >> 16) | (r[u][1][d] & 0xffff0000u);
-            w1 = (r[u][2][d] >> 16) | (r[u][3][d] & 0xffff0000u);
-          } else {
-            w0 = (r[u][0][d] & 0xffffu) | (r[u][1][d] << 16);
-            w1 = (r[u][2][d] & 0xffffu) | (r[u][3][d] << 16);
-          }
+          // v_perm_b32 picks bytes of {hi, lo}: 0-3 from lo, 4-7 from hi.
+          // Even e: low halves of the two rows, odd e: high halves.
+          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const unsigned w0 = __builtin_amdgcn_perm(r[u][1][d], r[u][0][d], sel);
+          const unsigned w1 = __builtin_amdgcn_perm(r[u][3][d], r[u][2][d], sel);
           *(u32x2*)(tm + tm_off(8 * tc + e, row, LDT)) = u32x2{w0, w1};
         }
       }
