@@ -27,17 +27,22 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
-// Tile shapes.  Wide tiles (64 queries per wave in the forward, 32 keys or
-// queries per wave in the backward) reuse each LDS fragment over more MFMAs;
-// small sequences use 16 per wave so that the grid still fills 256 CUs.
+// Tile shapes.  Wide tiles (the forward: 8 waves of 32 queries sharing one
+// K/V tile, at about 126 registers, so four waves fit a SIMD; the backward:
+// 4 waves of 32 keys or queries, two waves per SIMD) reuse each LDS fragment
+// over more MFMAs; small sequences use 16 per wave so that the grid still
+// fills 256 CUs.  (Measured: 8-wave backward workgroups were slower.)
 // 16-bit fragments (bf16, fp16) take half the registers of fp32 ones and
 // share one set of tiles.  Defaults can be overridden at build time
 // (-DPSA_BF16_FWD_QB=...) for tuning.
 #ifndef PSA_BF16_FWD_QB
-#define PSA_BF16_FWD_QB 4
+#define PSA_BF16_FWD_QB 2
 #endif
 #ifndef PSA_BF16_FWD_NW
-#define PSA_BF16_FWD_NW 4
+#define PSA_BF16_FWD_NW 8
+#endif
+#ifndef PSA_BF16_BWD_NW
+#define PSA_BF16_BWD_NW 4
 #endif
 #ifndef PSA_BF16_DKDV_KB
 #define PSA_BF16_DKDV_KB 2
@@ -66,17 +71,20 @@ template <int DK, int DV> constexpr bool wide_heads() { return DK + DV > 128; }
 template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
   static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = W ? 2 : PSA_BF16_FWD_QB, FWD_BN = 64;
+  static constexpr int BWD_NW = PSA_BF16_BWD_NW;
   static constexpr int DKDV_KB = W ? 1 : PSA_BF16_DKDV_KB, DKDV_BMQ = W ? 32 : PSA_BF16_DKDV_BMQ;
   static constexpr int DQ_QB = W ? 1 : PSA_BF16_DQ_QB, DQ_BN = W ? 32 : PSA_BF16_DQ_BN;
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
+  static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = 32;
 };
 template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
+  static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = W ? 32 : 64;
   static constexpr int DQ_QB = 1, DQ_BN = W ? 32 : 64;
 };
@@ -208,8 +216,9 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
             float scale, psa::PackView pv, hipStream_t st) {
   const float c = scale * psa::kLog2e;
   const long long total = (long long)BH * N;
-  constexpr int BNK = 4 * 16 * C::DKDV_KB;  // keys per dK/dV workgroup
-  constexpr int BMD = 4 * 16 * C::DQ_QB;    // queries per dQ workgroup
+  constexpr int NW = C::BWD_NW;              // waves per workgroup
+  constexpr int BNK = NW * 16 * C::DKDV_KB;  // keys per dK/dV workgroup
+  constexpr int BMD = NW * 16 * C::DQ_QB;    // queries per dQ workgroup
   const int nkt = (N + BNK - 1) / BNK, nqt = (N + BMD - 1) / BMD;
   if ((long long)BH * (nkt + nqt) > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_attn_bwd: grid too large");
   const int nkb = BH * nkt, nqb = BH * nqt;
@@ -231,34 +240,34 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   {
     TimedLaunch tl(K_MAIN, st);
     if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, true>), dim3(nkb), dim3(256),
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, true>), dim3(nkb), dim3(NW * 64),
                          0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
     else
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, 4, C::DKDV_BMQ, false>), dim3(nkb),
-                         dim3(256), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, false>), dim3(nkb),
+                         dim3(NW * 64), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
     rc = check_launch("psa_attn_bwd dK/dV launch");
   }
   if (rc == PSA_OK) {
     TimedLaunch tl(K_DQ, st);
     if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, true>), dim3(nqb), dim3(256), 0, st,
+      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, NW, C::DQ_BN, true>), dim3(nqb), dim3(NW * 64), 0, st,
                          (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale, pv);
     else
-      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, 4, C::DQ_BN, false>), dim3(nqb), dim3(256), 0,
+      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, NW, C::DQ_BN, false>), dim3(nqb), dim3(NW * 64), 0,
                          st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale, pv);
     rc = check_launch("psa_attn_bwd dQ launch");
   }
 #else
   {
     TimedLaunch tl(K_MAIN, st);
-    const dim3 grid((unsigned)(nkb + nqb)), block(256);
+    const dim3 grid((unsigned)(nkb + nqb)), block(NW * 64);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL(
-          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, true>), grid, block, 0,
+          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, true>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     else
       hipLaunchKernelGGL(
-          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, false>), grid, block, 0,
+          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, false>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     rc = check_launch("psa_attn_bwd launch");
   }

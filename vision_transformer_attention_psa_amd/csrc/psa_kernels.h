@@ -110,11 +110,15 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
   __syncthreads();
 
   const Frag<T> ones = ones_frag<T>();
-  float m[QB];
+  // m: running column maximum (log2 units, scale included); thr: the raw
+  // score above which a column has outgrown m by more than the slack.
+  float m[QB], thr[QB];
+  const float cinv = 1.f / c;
   f32x4 oacc[DV / 16][QB], lacc[QB];
 #pragma unroll
   for (int nb = 0; nb < QB; ++nb) {
     m[nb] = kNegInf;
+    thr[nb] = kNegInf;
     lacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -157,13 +161,16 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
       // Each lane checks only its own 8 rows against the running maximum
       // plus the slack; the exact column maximum (a reduction over the lane
       // groups) is formed only when some lane's scores outgrew it.
+      // (A chain of maxima, so that it maps onto three-operand max.)
       float mx[QB];
       bool grow = false;
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) {
-        mx[nb] = fmaxf(fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), fmaxf(s[0][nb][2], s[0][nb][3])),
-                       fmaxf(fmaxf(s[1][nb][0], s[1][nb][1]), fmaxf(s[1][nb][2], s[1][nb][3])));
-        grow |= mx[nb] * c > m[nb] + kRescaleSlack;
+        float v = fmaxf(fmaxf(s[0][nb][0], s[0][nb][1]), s[0][nb][2]);
+        v = fmaxf(fmaxf(v, s[0][nb][3]), s[1][nb][0]);
+        v = fmaxf(fmaxf(v, s[1][nb][1]), s[1][nb][2]);
+        mx[nb] = fmaxf(v, s[1][nb][3]);
+        grow |= mx[nb] > thr[nb];
       }
       if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
@@ -171,6 +178,7 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
           const float mn = fmaxf(m[nb], wave_max4(mx[nb]) * c);
           const float alpha = fast_exp2(m[nb] - mn);
           m[nb] = mn;
+          thr[nb] = (mn + kRescaleSlack) * cinv;
           lacc[nb] *= alpha;
 #pragma unroll
           for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] *= alpha;
@@ -613,19 +621,19 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
 // dK/dV workgroups are dispatched first and the shorter dQ ones fill the
 // machine behind them, so neither pass leaves a partly idle last wave of
 // workgroups on its own; both share one LDS allocation.
-template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, bool VECOK>
-__global__ __launch_bounds__(256) PSA_OCCUPANCY void psa_bwd_fused_kernel(
+template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, int NW, bool VECOK>
+__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_fused_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
     T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale,
     const PackView pv) {
-  constexpr int S1 = DkdvShape<T, DK, DV, KB, 4, BMQ>::SMEM, S2 = DqShape<T, DK, DV, QB, 4, BN>::SMEM;
+  constexpr int S1 = DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM, S2 = DqShape<T, DK, DV, QB, NW, BN>::SMEM;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S1 > S2 ? S1 : S2];
   const int b = block_id();
   if (b < n_kblocks)
-    bwd_dkdv_body<T, DK, DV, KB, 4, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
+    bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
                                                 xcd_remap(b, n_kblocks), smem);
   else
-    bwd_dq_body<T, DK, DV, QB, 4, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale, pv,
+    bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale, pv,
                                              xcd_remap(b - n_kblocks, n_qblocks), smem);
 }
 

@@ -22,7 +22,9 @@ from collections import defaultdict
 
 PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
              ("psa_bwd_fused_kernel", "bwd_main"), ("psa_bwd_dkdv_kernel", "bwd_main"),
-             ("psa_bwd_dq_kernel", "bwd_dq"))
+             ("psa_bwd_dq_kernel", "bwd_dq"), ("psa_conv_dx_kernel", "conv_dx"),
+             ("psa_conv_dw_reduce_kernel", "conv_dw_reduce"), ("psa_conv_dw_kernel", "conv_dw"),
+             ("psa_rows_copy_kernel", "rows_copy"))
 
 
 def short_name(kernel: str) -> str:
@@ -33,8 +35,8 @@ def short_name(kernel: str) -> str:
             m = re.search(pat + r"I(DF16b|DF16_|f)((?:Li\d+E)*)", kernel)
             if m:
                 dt = {"DF16b": "bf16", "DF16_": "f16"}.get(m.group(1), "f32")
-                dims = ",".join(re.findall(r"Li(\d+)E", m.group(2)))
-                return f"{slot}<{dt},{dims}>"
+                dims = re.findall(r"Li(\d+)E", m.group(2))
+                return f"{slot}<{','.join([dt] + dims)}>"
             return slot
     return kernel[:60]
 
