@@ -30,6 +30,9 @@ PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
 def short_name(kernel: str) -> str:
     """Slot name plus dtype and the kernel's integer template arguments
     (head dims, then tile parameters), e.g. bwd_main<bf16,64,64,2,64,2,64>."""
+    # rocprofv3 half-demangles some names: the mangled prefix DF16bLi32E
+    # (bf16, then the integer 32) comes out as "bool _Accum, int, E".
+    kernel = kernel.replace("<bool _Accum, int, E", "IDF16bLi32E")
     for pat, slot in PSA_SLOTS:
         if pat in kernel:
             m = re.search(pat + r"I(DF16b|DF16_|f)((?:Li\d+E)*)", kernel)
