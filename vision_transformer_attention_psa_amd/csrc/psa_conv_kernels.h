@@ -60,10 +60,13 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
   __shared__ __attribute__((aligned(16))) T smem[4 * BUF];
 
   const int tid = thread_id(), wv = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  // ci tiles innermost: the workgroups that read one dy tile are
+  // consecutive, so they run together on one XCD and share it through L2.
   const int blk = xcd_remap(block_id(), n_blocks);
   const int per_b = n_ntiles * n_citiles;
   const int b = blk / per_b, r = blk - b * per_b;
-  const int ci0 = (r / n_ntiles) * BT, n0 = (r - (r / n_ntiles) * n_ntiles) * BT;
+  const int nt = r / n_citiles;
+  const int ci0 = (r - nt * n_citiles) * BT, n0 = nt * BT;
   const T* dyb = dy + (size_t)b * cout * N;
   const int wr = (wv >> 1) * 64, wc = (wv & 1) * 64;  // this wave's rows (ci) and columns (n)
 
