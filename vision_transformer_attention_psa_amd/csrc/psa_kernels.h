@@ -276,6 +276,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   constexpr int KW = Shape::KW, BNK = Shape::BNK, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BMQ % 32 == 0, "query tile must be a multiple of 32");
+  static_assert(BMQ <= NT, "one statistics entry per thread");
   using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, DK + DV, 0, DK + DV>;
   using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK, DK + DV, 0, 0>;
   constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
@@ -338,7 +339,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
     const T* tm = tm_of(nat, sg);       // columns: Q channels, then dO channels
     const float* sl = snl + cur * BMQ;
     const float* sd = snd + cur * BMQ;
-    if (qt + 1 < nqt) sg.load(Qg, dOg, N, (qt + 1) * BMQ, tid);
+    // Prefetch the next tile (rows and its queries' statistics) into
+    // registers; they reach LDS after this tile's MFMAs.
+    float pnl = kNegInf, pnd = 0.f;
+    if (qt + 1 < nqt) {
+      sg.load(Qg, dOg, N, (qt + 1) * BMQ, tid);
+      const int q = (qt + 1) * BMQ + tid;
+      if (tid < BMQ && q < N) {  // padding queries: P = 0
+        pnl = nlq[q];
+        pnd = ndq[q];
+      }
+    }
 
 #pragma unroll
     for (int c2 = 0; c2 < BMQ / 32; ++c2) {
@@ -408,10 +419,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
     if (qt + 1 < nqt) {
       T* nx = smem + (cur ^ 1) * TILE;
       sg.store(nx, tm_of(nx, sg), tid);
-      const int q0 = (qt + 1) * BMQ;
-      for (int q = tid; q < BMQ; q += NT) {
-        snl[(cur ^ 1) * BMQ + q] = q0 + q < N ? nlq[q0 + q] : kNegInf;
-        snd[(cur ^ 1) * BMQ + q] = q0 + q < N ? ndq[q0 + q] : 0.f;
+      if (tid < BMQ) {
+        snl[(cur ^ 1) * BMQ + tid] = pnl;
+        snd[(cur ^ 1) * BMQ + tid] = pnd;
       }
     }
     __syncthreads();
