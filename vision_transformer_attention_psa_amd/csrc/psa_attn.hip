@@ -306,15 +306,17 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
     rc = check_launch("psa_qkv_conv_bwd dx launch");
   }
   if (rc != PSA_OK) return rc;
-  // dw: the (b, token chunk) sum is split into S ranges so that the tiles
-  // times S fill about two workgroups per CU, with >= 4 chunks per range.
+  // dw: the (b, token chunk) sum is split into S ranges so that tiles x S
+  // fills the two workgroups per CU that its 74 KB of LDS allow, rounded
+  // down: one more workgroup than the CUs hold would cost a second round.
+  // Each range keeps >= 4 chunks.
   constexpr int BT = psa::is_16bit<T>() ? 64 : 32;
   const long long nchunk = (long long)B * ((N + BT - 1) / BT);
   const int tiles = n_citiles * n_cotiles;
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(PSA_ERR_HIP, "psa_qkv_conv_bwd: device query failed");
-  long long S = (2LL * cus + tiles - 1) / tiles;
+  long long S = (2LL * cus) / tiles;
   S = std::min<long long>(S, std::max<long long>(1, nchunk / 4));
   S = std::max<long long>(1, std::min<long long>(S, 64));
   float* part = nullptr;
