@@ -172,6 +172,13 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _check_out(name: str, t, shape, dtype, device) -> None:
+    """Caller-provided outputs must be exactly what the library will write."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"out {name} must be a contiguous {tuple(shape)} {dtype} tensor on {device}; "
+                         f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+
+
 def psa_qkv_conv_bwd(x: int, w: int, dy: int, dx: int, dw: int, B: int, cin: int, cout: int, N: int,
                      dtype: int, stream: int | None) -> int:
     """Raw call with device addresses; returns the status code."""
@@ -212,6 +219,8 @@ def fwd(qkv, dk: int, dv: int, scale: float, out=None):
         lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
     else:
         o, lse = out
+        _check_out("o", o, (B, H, dv, N), qkv.dtype, qkv.device)
+        _check_out("lse", lse, (B, H, N), torch.float32, qkv.device)
     _check("psa_attn_fwd", psa_attn_fwd(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, dk,
                                         dv, float(scale), _dtype_code(qkv), _stream(qkv)))
     return o, lse
@@ -231,6 +240,7 @@ def bwd(qkv, o, lse, dO, dk: int, dv: int, scale: float, out=None):
     if o.dtype != qkv.dtype or dO.dtype != qkv.dtype:
         raise ValueError("o and dO must have qkv's dtype")
     d = torch.empty_like(qkv) if out is None else out
+    _check_out("d_packed", d, qkv.shape, qkv.dtype, qkv.device)
     _check("psa_attn_bwd", psa_attn_bwd(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), dO.data_ptr(),
                                         d.data_ptr(), B, H, N, dk, dv, float(scale),
                                         _dtype_code(qkv), _stream(qkv)))
@@ -258,6 +268,8 @@ def conv_bwd(x, w, dy, out=None):
         dw = torch.empty_like(w)
     else:
         dx, dw = out
+        _check_out("dx", dx, x.shape, x.dtype, x.device)
+        _check_out("dw", dw, w.shape, w.dtype, x.device)
     _check("psa_qkv_conv_bwd", psa_qkv_conv_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(),
                                                 dw.data_ptr(), B, cin, cout, N, _dtype_code(x), _stream(x)))
     return dx, dw
@@ -283,6 +295,11 @@ def conv_cat_bwd(x, w, dy, part_channels, out=None):
         dw = torch.empty_like(w)
     else:
         dxs, dw = out
+        if len(dxs) != len(part_channels):
+            raise ValueError("out must hold one dx tensor per part")
+        for k, (d_, c) in enumerate(zip(dxs, part_channels)):
+            _check_out(f"dx[{k}]", d_, (B, c, N), x.dtype, x.device)
+        _check_out("dw", dw, w.shape, w.dtype, x.device)
     _check("psa_qkv_conv_cat_bwd",
            psa_qkv_conv_cat_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), [d.data_ptr() for d in dxs],
                                 list(part_channels), dw.data_ptr(), B, cin, cout, N, _dtype_code(x),
@@ -326,6 +343,8 @@ def fwd_vslice(qkv, dk: int, dv_total: int, v0: int, dv: int, scale: float, out=
         lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
     else:
         o, lse = out
+        _check_out("o", o, (B, H, dv, N), qkv.dtype, qkv.device)
+        _check_out("lse", lse, (B, H, N), torch.float32, qkv.device)
     _check("psa_attn_fwd_vslice", psa_attn_fwd_vslice(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, dk,
                                                       dv_total, v0, dv, float(scale), _dtype_code(qkv),
                                                       _stream(qkv)))
@@ -366,6 +385,7 @@ def merge_fwd(o_lo, o_hi, out=None):
         raise ValueError("o_lo and o_hi must be contiguous")
     B, H, half, N = o_lo.shape
     m = torch.empty((B, H, 2 * half, N), dtype=o_lo.dtype, device=o_lo.device) if out is None else out
+    _check_out("merged", m, (B, H, 2 * half, N), o_lo.dtype, o_lo.device)
     _check("psa_merge_fwd", psa_merge_fwd(o_lo.data_ptr(), o_hi.data_ptr(), m.data_ptr(), B, H, N, half,
                                           _dtype_code(o_lo), _stream(o_lo)))
     return m
@@ -383,6 +403,8 @@ def merge_bwd(d_merged, out=None):
         hi = torch.empty_like(lo)
     else:
         lo, hi = out
+        _check_out("d_lo", lo, (B, H, half, N), d_merged.dtype, d_merged.device)
+        _check_out("d_hi", hi, (B, H, half, N), d_merged.dtype, d_merged.device)
     _check("psa_merge_bwd", psa_merge_bwd(d_merged.data_ptr(), lo.data_ptr(), hi.data_ptr(), B, H, N, half,
                                           _dtype_code(d_merged), _stream(d_merged)))
     return lo, hi

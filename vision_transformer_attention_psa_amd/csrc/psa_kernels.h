@@ -13,15 +13,19 @@
 //                    than 2^8), O^T += V^T P^T and the row sums l += 1 P^T,
 //                    all on MFMA.  Writes O and LSE.
 //   psa_bwd_pre      D_i = sum_c dO_ic O_ic and LSE in log2 units.
-//   psa_bwd_dkdv     one workgroup per (slice, tile of keys); keys stationary,
+//   bwd_dkdv_body    one workgroup per (slice, tile of keys); keys stationary,
 //                    query tiles streamed: S = Q K^T, dP = dO V^T,
 //                    P = exp(S - LSE), dS = P (dP - D), dV^T += dO^T P,
 //                    dK^T += Q^T dS.
-//   psa_bwd_dq       one workgroup per (slice, tile of queries); queries
+//   bwd_dq_body      one workgroup per (slice, tile of queries); queries
 //                    stationary, key tiles streamed: S^T, dP^T, dS^T as
 //                    above, dQ^T += K^T dS^T.
-// Every output element is written exactly once by one lane: no atomics, no
-// zero-initialisation, bitwise reproducible.
+//   psa_bwd_fused_kernel runs both bodies in one grid (dK/dV workgroups
+//                    first); psa_bwd_dkdv_kernel / psa_bwd_dq_kernel launch
+//                    them separately (a build option, for per-pass timing).
+// Every output element is written exactly once by one lane (with the
+// V-slice calls' accumulate flag: read, added to and written once): no
+// atomics, no zero-initialisation, bitwise reproducible.
 //
 // Orientation: outputs are accumulated transposed (channels as MFMA rows,
 // tokens as MFMA columns) so that accumulator lanes run along tokens and
