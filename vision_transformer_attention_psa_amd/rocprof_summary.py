@@ -2,6 +2,8 @@
 
   stats   <kernel_stats.csv> <out.md> --command "..."
           per-kernel call count / total / average / min / max duration
+  pmc     <counter_collection.csv>... --out <md> --command "..."
+          per-kernel counter averages and derived utilisation ratios
   traffic <fetch counter_collection.csv> <write counter_collection.csv>
           --workload NAME --copy-mib M --out-json profiles/traffic.json
           --out-md profiles/<...>.md --command "..."
@@ -111,6 +113,66 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, out_js
     print("\n".join(md))
 
 
+def pmc(csvs: list, out: str, command: str, cus: int = 256, xccs: int = 8) -> None:
+    """Per-kernel averages of the counters in one or more --pmc runs and the
+    ratios derived from them.  Utilisation expressions follow rocprofv3's own
+    derived metrics: MFMA busy = sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE
+    of one XCC x SIMDs); GRBM_GUI_ACTIVE in the CSV is the sum over the XCCs."""
+    vals = defaultdict(lambda: defaultdict(list))  # short name -> counter -> per-dispatch values
+    dur = defaultdict(dict)
+    for path in csvs:
+        per = defaultdict(lambda: defaultdict(float))
+        for r in csv.DictReader(open(path)):
+            name = short_name(r["Kernel_Name"])
+            if not any(p in r["Kernel_Name"] for p, _ in PSA_SLOTS):
+                continue
+            key = (name, r["Dispatch_Id"])
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            dur[name][(path, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        for (name, _), cs in per.items():
+            for c, v in cs.items():
+                vals[name][f"{c}@{path}" if c == "GRBM_GUI_ACTIVE" else c].append(v)
+    avg = {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in vals.items()}
+    simds = cus * 4
+
+    def div(x, y):
+        return x / y if y else float("nan")
+
+    def gui(a, counter_file):
+        return a.get(f"GRBM_GUI_ACTIVE@{counter_file}", float("nan")) / xccs
+
+    rows = []
+    for name in sorted(avg, key=lambda n: -sum(dur[n].values()) / max(1, len(dur[n]))):
+        a = avg[name]
+        f1 = next((p for p in csvs if f"GRBM_GUI_ACTIVE@{p}" in a and "SQ_INSTS_MFMA" in a), csvs[0])
+        mf = a.get("SQ_INSTS_MFMA", float("nan"))
+        g = gui(a, f1)
+        rows.append((name, sum(dur[name].values()) / len(dur[name]),
+                     100 * div(a.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")), g * simds),
+                     div(a.get("SQ_INSTS_VALU", float("nan")), mf),
+                     div(a.get("SQ_INSTS_VALU_TRANS_F32", float("nan")), mf),
+                     div(a.get("SQ_INSTS_LDS", float("nan")), mf),
+                     100 * div(a.get("SQ_LDS_BANK_CONFLICT", float("nan")), g * cus),
+                     100 * div(a.get("SQ_ACTIVE_INST_VALU", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan"))),
+                     100 * div(a.get("SQ_ACTIVE_INST_LDS", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan"))),
+                     100 * div(a.get("SQ_WAIT_ANY", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan")))))
+    lines = ["# rocprofv3 counters per kernel", "", f"Commands: `{command}`", "",
+             "Columns: MFMA busy = sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC x "
+             f"{simds} SIMDs); VALU/MFMA, TRANS/MFMA, LDS/MFMA = issued instructions per MFMA "
+             "instruction (SQ_INSTS_VALU counts MFMA too); LDS conflict = SQ_LDS_BANK_CONFLICT / "
+             f"(GRBM_GUI_ACTIVE per XCC x {cus} CUs); VALU / LDS active and waiting = SQ_ACTIVE_INST_VALU, "
+             "SQ_ACTIVE_INST_LDS and SQ_WAIT_ANY as a share of SQ_WAVE_CYCLES (wave-cycles, all in quad-cycles; "
+             "counters from two runs). Durations are per dispatch under the profiler.", "",
+             "| kernel | us | MFMA busy % | VALU/MFMA | TRANS/MFMA | LDS/MFMA | LDS conflict % | "
+             "VALU active % | LDS active % | waiting % |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| " + r[0] + " | " + " | ".join(f"{x:.1f}" if i in (0, 1, 5, 6, 7, 8) else f"{x:.2f}"
+                                                    for i, x in enumerate(r[1:])) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -127,8 +189,14 @@ def main() -> None:
     t.add_argument("--out-md", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--fingerprint", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("csv", nargs="+")
+    m.add_argument("--out", required=True)
+    m.add_argument("--command", required=True)
     a = ap.parse_args()
-    if a.cmd == "stats":
+    if a.cmd == "pmc":
+        pmc(a.csv, a.out, a.command)
+    elif a.cmd == "stats":
         stats(a.csv, a.out, a.command)
     else:
         traffic(a.fetch_csv, a.write_csv, a.workload, a.copy_mib, a.out_json, a.out_md, a.command,
