@@ -86,6 +86,14 @@ EDGE = [
     (inputs.BF16, 128, 128, 1, 1, 700),
     (inputs.F16, 128, 128, 1, 2, 97),
     (inputs.F16, 64, 128, 1, 1, 1000),
+    # (64, 32): the V halves at dk = dv = 64
+    (inputs.F32, 64, 32, 1, 1, 130),
+    (inputs.BF16, 64, 32, 1, 2, 97),
+    (inputs.F16, 64, 32, 2, 1, 700),
+    # the short/long tile switch (N <= 512 uses the narrow tiles)
+    (inputs.BF16, 32, 64, 1, 2, 512),
+    (inputs.BF16, 32, 64, 1, 2, 513),
+    (inputs.BF16, 64, 64, 1, 1, 512),
 ]
 
 
@@ -242,3 +250,31 @@ def test_invariants_at_full_size_highres():
     tot = x.dO.astype(np.float64).sum(axis=-1)
     scale = np.abs(dV).sum(axis=-1)
     assert (np.abs(dV.sum(axis=-1) - tot) <= 2e-2 * scale + 1e-6).all()
+
+
+def test_beyond_two_billion_elements():
+    """B*heads = 2048 slices at N = 6400, dk = dv = 64 (bf16): qkv holds
+    2.5e9 elements, so the last slices sit beyond any 32-bit element offset.
+    Inputs are seeded normals drawn on the device; the first and last slices
+    are copied to the host and checked against the oracle."""
+    t = torch()
+    B, H, N, dk, dv = 64, 32, 6400, 64, 64
+    assert B * H * (2 * dk + dv) * N > 2 ** 31
+    g = t.Generator(device="cuda").manual_seed(2024)
+    qkv = t.randn((B, H, 2 * dk + dv, N), generator=g, device="cuda", dtype=t.bfloat16)
+    dO = t.randn((B, H, dv, N), generator=g, device="cuda", dtype=t.bfloat16)
+    scale = 1.0 / 8.0
+    o, lse = binding.fwd(qkv, dk, dv, scale)
+    d = binding.bwd(qkv, o, lse, dO, dk, dv, scale)
+    t.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        q64 = qkv[b, h].float().cpu().numpy().astype(np.float64)[None, None]
+        g64 = dO[b, h].float().cpu().numpy().astype(np.float64)[None, None]
+        ro, rl, rd = orc.forward_backward(q64, g64, dk, dv, scale)
+        e = {"O": orc.max_rel_err(to_host(o[b, h])[None, None], ro),
+             "LSE": orc.max_rel_err(to_host(lse[b, h])[None, None], rl),
+             "d": orc.max_rel_err(to_host(d[b, h])[None, None], rd)}
+        print(f"slice ({b},{h})", {k: f"{v:.2e}" for k, v in e.items()}, flush=True)
+        assert max(e.values()) <= TOL[inputs.BF16], e
+    del qkv, dO, o, lse, d
+    t.cuda.empty_cache()
