@@ -408,3 +408,38 @@ def merge_bwd(d_merged, out=None):
     _check("psa_merge_bwd", psa_merge_bwd(d_merged.data_ptr(), lo.data_ptr(), hi.data_ptr(), B, H, N, half,
                                           _dtype_code(d_merged), _stream(d_merged)))
     return lo, hi
+
+
+def _autograd_function():
+    import torch
+
+    class PsaAttnFunction(torch.autograd.Function):
+        """O = PSA attention of the packed qkv [B, heads, 2dk+dv, N]; the
+        backward returns d_packed through psa_attn_bwd (deterministic)."""
+
+        @staticmethod
+        def forward(ctx, qkv, dk: int, dv: int, scale: float):
+            qkv = qkv.contiguous()
+            o, lse = fwd(qkv, dk, dv, scale)
+            ctx.save_for_backward(qkv, o, lse)
+            ctx.dims = (dk, dv, scale)
+            return o
+
+        @staticmethod
+        def backward(ctx, dO):
+            qkv, o, lse = ctx.saved_tensors
+            dk, dv, scale = ctx.dims
+            return bwd(qkv, o, lse, dO.contiguous(), dk, dv, scale), None, None, None
+
+    return PsaAttnFunction
+
+
+_FN = None
+
+
+def psa_attention(qkv, dk: int, dv: int, scale: float):
+    """Differentiable PSA attention: O [B, heads, dv, N] from qkv."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    return _FN.apply(qkv, dk, dv, scale)
