@@ -90,10 +90,12 @@ EDGE = [
     (inputs.F32, 64, 32, 1, 1, 130),
     (inputs.BF16, 64, 32, 1, 2, 97),
     (inputs.F16, 64, 32, 2, 1, 700),
-    # the short/long tile switch (N <= 512 uses the narrow tiles)
+    # the short/long tile switches (narrow tiles: forward N <= 512, backward N <= 256)
     (inputs.BF16, 32, 64, 1, 2, 512),
     (inputs.BF16, 32, 64, 1, 2, 513),
     (inputs.BF16, 64, 64, 1, 1, 512),
+    (inputs.BF16, 32, 64, 1, 2, 256),
+    (inputs.F16, 32, 64, 1, 2, 257),
 ]
 
 

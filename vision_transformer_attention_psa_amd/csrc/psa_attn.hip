@@ -60,7 +60,13 @@ int fail(int code, const std::string& msg) {
 #define PSA_BWD_SPLIT 0  // 1: separate dK/dV and dQ launches (per-pass timing)
 #endif
 #ifndef PSA_SMALL_N_MAX
-#define PSA_SMALL_N_MAX 512  // sequences up to this length use the narrow tiles
+#define PSA_SMALL_N_MAX 512  // forward: sequences up to this length use the narrow tiles
+#endif
+// Backward: measured at B*heads = 64 (dk 32, dv 64), the narrow tiles win up
+// to N = 256 (13.3 vs 13.9 us) and the wide ones from N = 320 (16.8 vs 17.8 us;
+// N = 400: 22.3 vs 24.2 us, N = 512: 24.2 vs 27.6 us).
+#ifndef PSA_SMALL_N_MAX_BWD
+#define PSA_SMALL_N_MAX_BWD 256
 #endif
 // Head dims with dk + dv > 128 ("wide heads") halve the per-wave register
 // tiles (their accumulators and stationary fragments are twice as large)
@@ -90,9 +96,8 @@ template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int DQ_QB = 1, DQ_BN = 32;
 };
 // Narrow backward: 32-query dK/dV tiles keep the kernel at about 113
-// registers and 36 KB of LDS, so four workgroups share a CU and the ~900
-// workgroups of a B*heads = 64, N = 400 call run in one round (measured 10%
-// faster than 64-query tiles at two workgroups per CU).
+// registers and 36 KB of LDS, so four workgroups share a CU (measured 10%
+// faster than 64-query tiles at two workgroups per CU, at N = 400).
 template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
@@ -538,7 +543,7 @@ int attn_bwd_impl(const char* fn, const void* qkv, const void* o, const float* l
   const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, accum ? 1 : 0};
 #define X(DT, T, K, V)                                                                                        \
   if (dtype == DT && dk == K && dv == V)                                                                      \
-    return N <= PSA_SMALL_N_MAX                                                                               \
+    return N <= PSA_SMALL_N_MAX_BWD                                                                           \
                ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st) \
                : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st);
   PSA_INSTANCES(X)
