@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 CSV output for the profiles/ directory.
 
-  stats   <kernel_stats.csv> <out.md> --command "..."
-          per-kernel call count / total / average / min / max duration
+  stats   <kernel_stats.csv> <out.md> --command "..." [--trace <kernel_trace.csv>]
+          per-kernel (or per kernel and grid) call count / total / average /
+          min / max duration
   pmc     <counter_collection.csv>... --out <md> --command "..."
           per-kernel counter averages and derived utilisation ratios
   traffic <fetch counter_collection.csv> <write counter_collection.csv>
@@ -46,17 +47,31 @@ def short_name(kernel: str) -> str:
     return kernel[:60]
 
 
-def stats(path: str, out: str, command: str) -> None:
-    rows = list(csv.DictReader(open(path)))
-    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
-             "| kernel | calls | total us | avg us | min us | max us | % |",
-             "|---|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
-        ns = lambda k: float(r[k]) / 1000.0
-        lines.append(f"| {short_name(name)} | {r['Calls']} | {ns('TotalDurationNs'):.1f} | "
-                     f"{ns('AverageNs'):.1f} | {ns('MinNs'):.1f} | {ns('MaxNs'):.1f} | "
-                     f"{float(r['Percentage']):.1f} |")
+def stats(path: str, out: str, command: str, trace: str | None = None) -> None:
+    """One row per kernel from the stats CSV; with the kernel-trace CSV, one
+    row per (kernel, grid size), so that one instance used by two workloads
+    shows as two rows."""
+    lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{command}`", ""]
+    if trace:
+        per = defaultdict(list)
+        for r in csv.DictReader(open(trace)):
+            grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            per[(short_name(r["Kernel_Name"]), grid)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        tot = sum(sum(v) for v in per.values())
+        lines += ["| kernel | workgroups | calls | total us | avg us | min us | max us | % |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for (name, grid), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| {name} | {grid} | {len(v)} | {sum(v):.1f} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+                         f"{max(v):.1f} | {100 * sum(v) / tot:.1f} |")
+    else:
+        lines += ["| kernel | calls | total us | avg us | min us | max us | % |",
+                  "|---|---|---|---|---|---|---|"]
+        for r in csv.DictReader(open(path)):
+            name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+            ns = lambda k: float(r[k]) / 1000.0
+            lines.append(f"| {short_name(name)} | {r['Calls']} | {ns('TotalDurationNs'):.1f} | "
+                         f"{ns('AverageNs'):.1f} | {ns('MinNs'):.1f} | {ns('MaxNs'):.1f} | "
+                         f"{float(r['Percentage']):.1f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -180,6 +195,7 @@ def main() -> None:
     s.add_argument("csv")
     s.add_argument("out")
     s.add_argument("--command", required=True)
+    s.add_argument("--trace", help="kernel_trace.csv of the same run: one row per (kernel, grid size)")
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
@@ -197,7 +213,7 @@ def main() -> None:
     if a.cmd == "pmc":
         pmc(a.csv, a.out, a.command)
     elif a.cmd == "stats":
-        stats(a.csv, a.out, a.command)
+        stats(a.csv, a.out, a.command, a.trace)
     else:
         traffic(a.fetch_csv, a.write_csv, a.workload, a.copy_mib, a.out_json, a.out_md, a.command,
                 a.fingerprint)
