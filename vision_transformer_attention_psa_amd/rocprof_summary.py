@@ -138,9 +138,11 @@ def pmc(csvs: list, out: str, command: str, cus: int = 256, xccs: int = 8) -> No
     for path in csvs:
         per = defaultdict(lambda: defaultdict(float))
         for r in csv.DictReader(open(path)):
-            name = short_name(r["Kernel_Name"])
             if not any(p in r["Kernel_Name"] for p, _ in PSA_SLOTS):
                 continue
+            # one row per (kernel, workgroups): an instance shared by two workloads shows twice
+            wg = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            name = f"{short_name(r['Kernel_Name'])} x{wg}"
             key = (name, r["Dispatch_Id"])
             per[key][r["Counter_Name"]] += float(r["Counter_Value"])
             dur[name][(path, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
@@ -170,18 +172,22 @@ def pmc(csvs: list, out: str, command: str, cus: int = 256, xccs: int = 8) -> No
                      100 * div(a.get("SQ_LDS_BANK_CONFLICT", float("nan")), g * cus),
                      100 * div(a.get("SQ_ACTIVE_INST_VALU", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan"))),
                      100 * div(a.get("SQ_ACTIVE_INST_LDS", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan"))),
-                     100 * div(a.get("SQ_WAIT_ANY", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan")))))
+                     100 * div(a.get("SQ_WAIT_ANY", float("nan")), a.get("SQ_WAVE_CYCLES", float("nan"))),
+                     100 * div(a.get("TCC_HIT_sum", float("nan")),
+                               a.get("TCC_HIT_sum", float("nan")) + a.get("TCC_MISS_sum", float("nan")))))
     lines = ["# rocprofv3 counters per kernel", "", f"Commands: `{command}`", "",
              "Columns: MFMA busy = sum SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC x "
              f"{simds} SIMDs); VALU/MFMA, TRANS/MFMA, LDS/MFMA = issued instructions per MFMA "
              "instruction (SQ_INSTS_VALU counts MFMA too); LDS conflict = SQ_LDS_BANK_CONFLICT / "
              f"(GRBM_GUI_ACTIVE per XCC x {cus} CUs); VALU / LDS active and waiting = SQ_ACTIVE_INST_VALU, "
-             "SQ_ACTIVE_INST_LDS and SQ_WAIT_ANY as a share of SQ_WAVE_CYCLES (wave-cycles, all in quad-cycles; "
-             "counters from two runs). Durations are per dispatch under the profiler.", "",
-             "| kernel | us | MFMA busy % | VALU/MFMA | TRANS/MFMA | LDS/MFMA | LDS conflict % | "
-             "VALU active % | LDS active % | waiting % |", "|---|---|---|---|---|---|---|---|---|---|"]
+             "SQ_ACTIVE_INST_LDS and SQ_WAIT_ANY as a share of SQ_WAVE_CYCLES (wave-cycles, all in quad-cycles); "
+             "L2 hit = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum), all L2 requests of the dispatch. Counters "
+             "come from separate runs; durations are per dispatch under the profiler.", "",
+             "| kernel x workgroups | us | MFMA busy % | VALU/MFMA | TRANS/MFMA | LDS/MFMA | LDS conflict % | "
+             "VALU active % | LDS active % | waiting % | L2 hit % |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append("| " + r[0] + " | " + " | ".join(f"{x:.1f}" if i in (0, 1, 5, 6, 7, 8) else f"{x:.2f}"
+        lines.append("| " + r[0] + " | " + " | ".join(f"{x:.1f}" if i in (0, 1, 5, 6, 7, 8, 9) else f"{x:.2f}"
                                                     for i, x in enumerate(r[1:])) + " |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
