@@ -41,6 +41,9 @@ int fail(int code, const std::string& msg) {
 #ifndef PSA_BF16_FWD_NW
 #define PSA_BF16_FWD_NW 8
 #endif
+#ifndef PSA_BF16_FWD_BN
+#define PSA_BF16_FWD_BN 64  // 128-key tiles measured 16% slower at N = 6400
+#endif
 #ifndef PSA_BF16_BWD_NW
 #define PSA_BF16_BWD_NW 4
 #endif
@@ -55,6 +58,12 @@ int fail(int code, const std::string& msg) {
 #endif
 #ifndef PSA_BF16_DQ_BN
 #define PSA_BF16_DQ_BN 64
+#endif
+// dK/dV body: query tiles prefetched two iterations ahead (the thread halves
+// take turns).  Measured -4% at N = 400, -3% at N = 1600, -0.7% at N = 6400;
+// the same for the dQ body's and the forward's key tiles measured no gain.
+#ifndef PSA_DKDV_DEEP
+#define PSA_DKDV_DEEP 1
 #endif
 #ifndef PSA_BWD_SPLIT
 #define PSA_BWD_SPLIT 0  // 1: separate dK/dV and dQ launches (per-pass timing)
@@ -76,7 +85,7 @@ template <int DK, int DV> constexpr bool wide_heads() { return DK + DV > 128; }
 
 template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
-  static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = W ? 2 : PSA_BF16_FWD_QB, FWD_BN = 64;
+  static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = W ? 2 : PSA_BF16_FWD_QB, FWD_BN = W ? 64 : PSA_BF16_FWD_BN;
   static constexpr int BWD_NW = PSA_BF16_BWD_NW;
   // dk = 32: 32-query dK/dV tiles bring the kernel to about 162 registers,
   // three waves per SIMD (measured 5% faster at N = 1600); dk = 64 stays at
@@ -88,12 +97,14 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   // of each K/V fragment (measured 3% faster at N = 6400); at dk = 32 the
   // extra registers would cost a wave per SIMD.
   static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? PSA_BF16_DQ_QB : 3), DQ_BN = W ? 32 : PSA_BF16_DQ_BN;
+  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP;
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
   static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = 32;
+  static constexpr bool DKDV_DEEP = false;
 };
 // Narrow backward: 32-query dK/dV tiles keep the kernel at about 113
 // registers and 36 KB of LDS, so four workgroups share a CU (measured 10%
@@ -104,6 +115,7 @@ template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
   static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = W ? 32 : 64;
+  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP;
 };
 template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, DK, DV> {};
 
@@ -257,10 +269,10 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   {
     TimedLaunch tl(K_MAIN, st);
     if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, true>), dim3(nkb), dim3(NW * 64),
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, true, C::DKDV_DEEP>), dim3(nkb), dim3(NW * 64),
                          0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
     else
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, false>), dim3(nkb),
+      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, false, C::DKDV_DEEP>), dim3(nkb),
                          dim3(NW * 64), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
     rc = check_launch("psa_attn_bwd dK/dV launch");
   }
@@ -280,11 +292,11 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     const dim3 grid((unsigned)(nkb + nqb)), block(NW * 64);
     if (vec_ok<T>(N))
       hipLaunchKernelGGL(
-          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, true>), grid, block, 0,
+          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, true, C::DKDV_DEEP>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     else
       hipLaunchKernelGGL(
-          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, false>), grid, block, 0,
+          (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, false, C::DKDV_DEEP>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     rc = check_launch("psa_attn_bwd launch");
   }

@@ -270,7 +270,7 @@ struct DkdvShape {
   static constexpr int SMEM = QG_BYTES > KV_BYTES ? QG_BYTES : KV_BYTES;
 };
 
-template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
+template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK, bool DEEP = false>
 __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T* __restrict__ dO,
                                               const float* __restrict__ nlg, const float* __restrict__ ndg,
                                               T* __restrict__ dpk, int N,
@@ -336,23 +336,43 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   }
   __syncthreads();
 
+  // DEEP: the two thread halves take turns, each keeping one tile in flight
+  // in its registers from the top of iteration qt to the end of qt + 1: a
+  // prefetch distance of two tiles, at the register cost of one wherever a
+  // tile needs no more than half the threads.
+  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK, DK + DV, 0, DK + DV>;
+  static_assert(!DEEP || BMQ <= NT / 2, "one statistics entry per thread of a half");
+  const int half = tid >= NT / 2, htid = tid - half * (NT / 2);
+  SQH sh;
+  float pnl = kNegInf, pnd = 0.f;
+  auto load_tile = [&](int qt, int lt) {  // rows and statistics of query tile qt (lt = thread index)
+    if constexpr (DEEP)
+      sh.load(Qg, dOg, N, qt * BMQ, lt);
+    else
+      sg.load(Qg, dOg, N, qt * BMQ, lt);
+    const int q = qt * BMQ + lt;
+    pnl = kNegInf, pnd = 0.f;
+    if (lt < BMQ && q < N) {  // padding queries: P = 0
+      pnl = nlq[q];
+      pnd = ndq[q];
+    }
+  };
   const int nqt = (N + BMQ - 1) / BMQ;
+  if constexpr (DEEP) {
+    if (half == 1 && 1 < nqt) load_tile(1, htid);
+  }
   for (int qt = 0; qt < nqt; ++qt) {
     const int cur = qt & 1;
     const T* nat = smem + cur * TILE;   // rows: Q channels, then dO channels
     const T* tm = tm_of(nat, sg);       // columns: Q channels, then dO channels
     const float* sl = snl + cur * BMQ;
     const float* sd = snd + cur * BMQ;
-    // Prefetch the next tile (rows and its queries' statistics) into
+    // Prefetch a later tile (rows and its queries' statistics) into
     // registers; they reach LDS after this tile's MFMAs.
-    float pnl = kNegInf, pnd = 0.f;
-    if (qt + 1 < nqt) {
-      sg.load(Qg, dOg, N, (qt + 1) * BMQ, tid);
-      const int q = (qt + 1) * BMQ + tid;
-      if (tid < BMQ && q < N) {  // padding queries: P = 0
-        pnl = nlq[q];
-        pnd = ndq[q];
-      }
+    if constexpr (DEEP) {
+      if (qt + 2 < nqt && half == cur) load_tile(qt + 2, htid);
+    } else {
+      if (qt + 1 < nqt) load_tile(qt + 1, tid);
     }
 
 #pragma unroll
@@ -420,12 +440,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
       }
     }
 
-    if (qt + 1 < nqt) {
+    if (qt + 1 < nqt && (!DEEP || half != cur)) {
       T* nx = smem + (cur ^ 1) * TILE;
-      sg.store(nx, tm_of(nx, sg), tid);
-      if (tid < BMQ) {
-        snl[(cur ^ 1) * BMQ + tid] = pnl;
-        snd[(cur ^ 1) * BMQ + tid] = pnd;
+      const int lt = DEEP ? htid : tid;
+      if constexpr (DEEP)
+        sh.store(nx, tm_of(nx, sg), lt);
+      else
+        sg.store(nx, tm_of(nx, sg), lt);
+      if (lt < BMQ) {
+        snl[(cur ^ 1) * BMQ + lt] = pnl;
+        snd[(cur ^ 1) * BMQ + lt] = pnd;
       }
     }
     __syncthreads();
@@ -612,13 +636,13 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 }
 
 // ========================================================= backward kernels
-template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK>
+template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK, bool DEEP>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dkdv_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
     T* __restrict__ dpk, int N, int n_ktiles, int n_blocks, float c, float scale, const PackView pv) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM];
-  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
-                                               xcd_remap(block_id(), n_blocks), smem);
+  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK, DEEP>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
+                                                     xcd_remap(block_id(), n_blocks), smem);
 }
 
 template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
@@ -635,7 +659,7 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
 // dK/dV workgroups are dispatched first and the shorter dQ ones fill the
 // machine behind them, so neither pass leaves a partly idle last wave of
 // workgroups on its own; both share one LDS allocation.
-template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, int NW, bool VECOK>
+template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, int NW, bool VECOK, bool DEEP>
 __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_fused_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
     T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale,
@@ -644,8 +668,8 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_fused_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char smem[S1 > S2 ? S1 : S2];
   const int b = block_id();
   if (b < n_kblocks)
-    bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
-                                                xcd_remap(b, n_kblocks), smem);
+    bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK, DEEP>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
+                                                      xcd_remap(b, n_kblocks), smem);
   else
     bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale, pv,
                                              xcd_remap(b - n_kblocks, n_qblocks), smem);
