@@ -87,6 +87,15 @@ def per_dispatch(path: str, counter: str) -> dict:
     return {k: list(v.values()) for k, v in acc.items()}
 
 
+def _instance_prefixes(workload: str) -> dict:
+    """Short-name prefix of the kernel instance each slot runs for `workload`
+    (attention kernels carry (dk, dv), the preprocessing kernel dv)."""
+    from vision_transformer_attention_psa_amd.inputs import WORKLOADS
+    wl = WORKLOADS[workload]
+    return {"fwd": f"fwd<{wl.dtype},{wl.dk},{wl.dv},", "bwd_main": f"bwd_main<{wl.dtype},{wl.dk},{wl.dv},",
+            "bwd_dq": f"bwd_dq<{wl.dtype},{wl.dk},{wl.dv},", "bwd_pre": f"bwd_pre<{wl.dtype},{wl.dv}>"}
+
+
 def traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, out_json: str,
             out_md: str, command: str, fingerprint: str) -> None:
     f = per_dispatch(fetch_csv, "FETCH_SIZE")
@@ -99,13 +108,18 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, out_js
     w_cal = max(w[[k for k in w if "MulFunctor" in k][0]])
     f_scale, w_scale = known / f_cal, known / w_cal
     res, lines = {}, []
+    wanted = _instance_prefixes(workload)
     for k in f:
         slot = next((s for p, s in PSA_SLOTS if p in k), None)
         if slot is None:
             continue
         fb = sum(f[k]) / len(f[k]) * f_scale
         wb = sum(w.get(k, [0.0])) / max(1, len(w.get(k, []))) * w_scale
-        res[slot] = fb + wb
+        # Several instances of one slot can run in the same program (the
+        # V-slice calls use other head dims): record the workload's own.
+        pre = wanted.get(slot)
+        if slot not in res and (pre is None or short_name(k).startswith(pre)):
+            res[slot] = fb + wb
         lines.append(f"| {short_name(k)} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {(fb + wb) / 1e6:.2f} |")
     rec = {}
     if os.path.exists(out_json):
