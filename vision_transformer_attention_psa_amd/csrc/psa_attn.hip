@@ -260,8 +260,14 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   int rc;
   {
     TimedLaunch tl(K_PRE, st);
-    hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                       (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+    if (vec_ok<T>(N)) {  // 16-byte token groups x 8 channel groups, 256 lanes per 256 x 16 bytes of tokens
+      const long long lanes = total / (16 / (long long)sizeof(T)) * 8;
+      hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV, true>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0,
+                         st, (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+    } else {
+      hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV, false>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                         st, (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+    }
     rc = check_launch("psa_attn_bwd preprocess launch");
   }
   if (rc != PSA_OK) return rc;

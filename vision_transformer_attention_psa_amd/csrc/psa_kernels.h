@@ -238,20 +238,68 @@ __global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T*
 // LSE log2 e) and dP - D), and stored negated they enter an FMA or an MFMA
 // accumulator input as they are; four consecutive queries are one 16-byte
 // LDS read.
-template <typename T, int DV>
+//
+// VEC = false: one thread per query, walking the dv channels.
+// VEC = true (N a multiple of the 16-byte vector): lane (tg, cg) of a wave
+// owns the 16-byte token group tg (8 bf16/fp16 or 4 fp32 tokens) and the
+// channel group cg (dv / 8 channels), so that each lane issues all its loads
+// at once; the 8 channel groups' partial sums are then added across lanes.
+template <typename T, int DV, bool VEC>
 __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO,
                                                           const float* __restrict__ lse, float* __restrict__ stats,
                                                           int N, int total) {
-  const int idx = block_id() * 256 + thread_id();
-  if (idx >= total) return;
-  const int bh = idx / N, i = idx - bh * N;
-  const T* op = o + (size_t)bh * DV * N + i;
-  const T* gp = dO + (size_t)bh * DV * N + i;
-  float d = 0.f;
+  if constexpr (!VEC) {
+    const int idx = block_id() * 256 + thread_id();
+    if (idx >= total) return;
+    const int bh = idx / N, i = idx - bh * N;
+    const T* op = o + (size_t)bh * DV * N + i;
+    const T* gp = dO + (size_t)bh * DV * N + i;
+    float d = 0.f;
 #pragma unroll 16
-  for (int ch = 0; ch < DV; ++ch) d = __builtin_fmaf(to_f32(op[(size_t)ch * N]), to_f32(gp[(size_t)ch * N]), d);
-  stats[idx] = -lse[idx] * kLog2e;
-  stats[(size_t)total + idx] = -d;
+    for (int ch = 0; ch < DV; ++ch) d = __builtin_fmaf(to_f32(op[(size_t)ch * N]), to_f32(gp[(size_t)ch * N]), d);
+    stats[idx] = -lse[idx] * kLog2e;
+    stats[(size_t)total + idx] = -d;
+  } else {
+    constexpr int TV = 16 / (int)sizeof(T), NCG = 8, CPT = DV / NCG;
+    static_assert(DV % NCG == 0, "channel groups");
+    typedef T V __attribute__((ext_vector_type(TV)));
+    const int tid = thread_id(), lane = tid & 63, tg = lane & 7, cg = lane >> 3;
+    const int grp = (block_id() * 4 + (tid >> 6)) * 8 + tg;  // 16-byte token group
+    const int gpr = N / TV;                                   // token groups per slice
+    const bool live = grp < total / TV;
+    float d[TV];
+#pragma unroll
+    for (int e = 0; e < TV; ++e) d[e] = 0.f;
+    if (live) {
+      const int bh = grp / gpr, i0 = (grp - bh * gpr) * TV;
+      const size_t base = ((size_t)bh * DV + cg * CPT) * N + i0;
+      V ov[CPT], gv[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        ov[c] = *(const V*)(o + base + (size_t)c * N);
+        gv[c] = *(const V*)(dO + base + (size_t)c * N);
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int e = 0; e < TV; ++e) d[e] = __builtin_fmaf(to_f32<T>(ov[c][e]), to_f32<T>(gv[c][e]), d[e]);
+    }
+    // Channel groups are lane bits 3..5: add across them (every lane active).
+#pragma unroll
+    for (int e = 0; e < TV; ++e) {
+      d[e] += __shfl_xor(d[e], 8);
+      d[e] += __shfl_xor(d[e], 16);
+      d[e] += __shfl_xor(d[e], 32);
+    }
+    if (live && cg == 0) {
+      const size_t q0 = (size_t)grp * TV;
+#pragma unroll
+      for (int e = 0; e < TV; ++e) {
+        stats[q0 + e] = -lse[q0 + e] * kLog2e;
+        stats[(size_t)total + q0 + e] = -d[e];
+      }
+    }
+  }
 }
 
 // ============================================================ backward dK/dV
