@@ -96,6 +96,13 @@ EDGE = [
     (inputs.BF16, 64, 64, 1, 1, 512),
     (inputs.BF16, 32, 64, 1, 2, 256),
     (inputs.F16, 32, 64, 1, 2, 257),
+    # the dK/dV two-deep prefetch: two query tiles only, a ragged last tile at dk = 64 (two
+    # register sets per thread half), many tiles; the vectorised preprocessing at N % 8 = 4
+    (inputs.BF16, 32, 64, 1, 1, 50),
+    (inputs.BF16, 64, 64, 1, 1, 300),
+    (inputs.BF16, 64, 64, 2, 1, 384),
+    (inputs.F16, 32, 64, 1, 1, 320),
+    (inputs.F32, 32, 64, 1, 1, 36),
 ]
 
 
