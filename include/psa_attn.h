@@ -82,7 +82,11 @@ int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N,
  *                  run to run; no floating-point atomics)
  * Scratch: 8*B*heads*N bytes of device memory from a grow-only buffer the
  * library keeps per (device, stream) until the process ends; the first call
- * on a stream (or a larger one) allocates it with hipMalloc.
+ * on a stream (or a larger one) allocates it with hipMalloc.  Under HIP graph
+ * capture: make one uncaptured call of at least the captured size on that
+ * stream first (capture cannot allocate), and do not make a larger call on
+ * that stream while the graph is in use (growing frees the buffer the graph
+ * refers to).
  */
 int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dO,
                  void* d_packed, int B, int heads, int N, int dk, int dv, float scale,
