@@ -168,7 +168,13 @@ def _check(fn: str, rc: int) -> None:
 
 
 def _stream(t) -> int:
+    """Handle of torch's current stream on t's device.  torch's raw accessor
+    returns it without building a Stream object (about 2 us per call less);
+    the public call is the fallback."""
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.device.index if t.device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
