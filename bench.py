@@ -217,6 +217,48 @@ def time_workload_graph(torch, wl, steps: int, warmup: int) -> dict:
     return {"fwd_us": fwd_us, "bwd_us": bwd_us, "bwd_tflops": fl["bwd"] / (bwd_us * 1e-6) / 1e12}
 
 
+COLD_FLUSH_MIB = 512  # twice the 256 MB last-level cache (Infinity Cache)
+
+
+def time_workload_cold(torch, wl, steps: int) -> dict:
+    """Each fwd and bwd call timed alone with hipEvents right after a 512 MiB
+    buffer was overwritten, so that none of its inputs (nor O, LSE) is left
+    in L2 or the last-level cache ("cold"), and the same loop without the
+    overwrite ("warm_same_events"): each call carries one event pair, which
+    at a few microseconds per call adds a visible share to both."""
+    from vision_transformer_attention_psa_amd import binding, inputs
+    x = inputs.make_inputs(wl)
+    qkv, dO = device_inputs(torch, x)
+    o = torch.empty((wl.B, wl.heads, wl.dv, wl.N), dtype=qkv.dtype, device="cuda")
+    lse = torch.empty((wl.B, wl.heads, wl.N), dtype=torch.float32, device="cuda")
+    d = torch.empty_like(qkv)
+    flush = torch.empty(COLD_FLUSH_MIB << 20, dtype=torch.uint8, device="cuda")
+    binding.psa_attn_timing_enable(False)
+    binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+    binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+    res = {}
+    for mode in ("cold", "warm_same_events"):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for e in ev:
+            if mode == "cold":
+                flush.fill_(1)
+            e[0].record()
+            binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+            e[1].record()
+            if mode == "cold":
+                flush.fill_(2)
+            e[2].record()
+            binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+            e[3].record()
+        torch.cuda.synchronize()
+        fwd_us = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3 / steps
+        bwd_us = sum(e[2].elapsed_time(e[3]) for e in ev) * 1e3 / steps
+        res[mode] = {"fwd_us": fwd_us, "bwd_us": bwd_us,
+                     "bwd_tflops": flops(wl)["bwd"] / (bwd_us * 1e-6) / 1e12}
+    res["flush_mib"] = COLD_FLUSH_MIB
+    return res
+
+
 def time_conv(torch, wl, steps: int, warmup: int) -> dict:
     """Backward of the block's qkv projection (a 1x1 convolution) at the
     workload's shape: x [B, heads*dv, N], w [heads*(2dk+dv), heads*dv], dy the
@@ -461,6 +503,12 @@ def main() -> int:
             graph[name] = time_workload_graph(torch, inputs.WORKLOADS[name], args.steps, args.warmup)
             print(f"[bench] graph replay {name}: fwd {graph[name]['fwd_us']:.1f} us, "
                   f"bwd {graph[name]['bwd_us']:.1f} us", file=sys.stderr, flush=True)
+    cold = {}
+    for name in [wl.name] + [a for a in args.also.split(",") if a]:
+        cold[name] = time_workload_cold(torch, inputs.WORKLOADS[name], args.steps)
+        c, w = cold[name]["cold"], cold[name]["warm_same_events"]
+        print(f"[bench] cold caches {name}: fwd {c['fwd_us']:.1f} us, bwd {c['bwd_us']:.1f} us "
+              f"(warm, same events: {w['fwd_us']:.1f} / {w['bwd_us']:.1f} us)", file=sys.stderr, flush=True)
     conv = time_conv(torch, wl, args.steps, args.warmup)
     print(f"[bench] qkv 1x1-conv backward {conv['shape']}: {conv['us_per_call']:.1f} us, "
           f"{conv['tflops']:.1f} TFLOP/s, kernels {conv['kernel_avg_us']}", file=sys.stderr, flush=True)
@@ -505,6 +553,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "also": also,
         "graph_replay": graph,
+        "cold_caches": cold,
         "qkv_conv_bwd": conv,
         "channel_cat_bwd": cat,
         "lo_hi_two_call": lohi,
