@@ -466,6 +466,9 @@ def main() -> int:
     ap.add_argument("--also", default=",".join(ALSO), help="comma list of extra workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--graph", type=int, default=1, help="also time HIP-graph replay of the step (1/0)")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="also time each call after overwriting 512 MiB (cold caches; 1/0). Off by default "
+                         "so that a profile of the default command holds warm calls only")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one plain MIB-MiB device copy first (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -504,7 +507,7 @@ def main() -> int:
             print(f"[bench] graph replay {name}: fwd {graph[name]['fwd_us']:.1f} us, "
                   f"bwd {graph[name]['bwd_us']:.1f} us", file=sys.stderr, flush=True)
     cold = {}
-    for name in [wl.name] + [a for a in args.also.split(",") if a]:
+    for name in ([wl.name] + [a for a in args.also.split(",") if a]) if args.cold else []:
         cold[name] = time_workload_cold(torch, inputs.WORKLOADS[name], args.steps)
         c, w = cold[name]["cold"], cold[name]["warm_same_events"]
         print(f"[bench] cold caches {name}: fwd {c['fwd_us']:.1f} us, bwd {c['bwd_us']:.1f} us "

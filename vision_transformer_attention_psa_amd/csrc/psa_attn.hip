@@ -50,6 +50,9 @@ int fail(int code, const std::string& msg) {
 #ifndef PSA_BF16_DKDV_KB
 #define PSA_BF16_DKDV_KB 2
 #endif
+#ifndef PSA_BF16_DKDV_KB_DK64
+#define PSA_BF16_DKDV_KB_DK64 3
+#endif
 #ifndef PSA_BF16_DKDV_BMQ
 #define PSA_BF16_DKDV_BMQ 64
 #endif
@@ -90,14 +93,18 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   // dk = 32: 32-query dK/dV tiles bring the kernel to about 162 registers,
   // three waves per SIMD (measured 5% faster at N = 1600); dk = 64 stays at
   // two waves per SIMD either way and runs faster with 64-query tiles.
-  static constexpr int DKDV_KB = W ? 1 : PSA_BF16_DKDV_KB;
+  // dk = 64: 48 keys per dK/dV wave (each streamed Q/dO fragment feeds three
+  // MFMAs instead of two) at 246 registers, with the one-tile prefetch (the
+  // two-deep one would need 270): 1126 vs 1168 us at N = 6400.  At dk = 32
+  // the 32-key waves with the two-deep prefetch stay faster.
+  static constexpr int DKDV_KB = W ? 1 : (DK <= 32 ? PSA_BF16_DKDV_KB : PSA_BF16_DKDV_KB_DK64);
   static constexpr int DKDV_BMQ = W ? 32 : (DK <= 32 ? 32 : PSA_BF16_DKDV_BMQ);
-  // dk = 64: 48 queries per dQ wave fit the registers the dK/dV body already
-  // needs (224), so the launch keeps two waves per SIMD with 1.5x the reuse
+  // dk = 64: 48 queries per dQ wave fit within the registers the dK/dV body
+  // already needs, so the launch keeps two waves per SIMD with 1.5x the reuse
   // of each K/V fragment (measured 3% faster at N = 6400); at dk = 32 the
   // extra registers would cost a wave per SIMD.
   static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? PSA_BF16_DQ_QB : 3), DQ_BN = W ? 32 : PSA_BF16_DQ_BN;
-  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP;
+  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && DKDV_KB <= 2;
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
