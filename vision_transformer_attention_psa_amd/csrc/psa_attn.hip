@@ -44,6 +44,9 @@ int fail(int code, const std::string& msg) {
 #ifndef PSA_BF16_FWD_BN
 #define PSA_BF16_FWD_BN 64  // 128-key tiles measured 16% slower at N = 6400
 #endif
+#ifndef PSA_FWD_DK64_48
+#define PSA_FWD_DK64_48 1
+#endif
 #ifndef PSA_BF16_BWD_NW
 #define PSA_BF16_BWD_NW 4
 #endif
@@ -88,7 +91,13 @@ template <int DK, int DV> constexpr bool wide_heads() { return DK + DV > 128; }
 
 template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
-  static constexpr int FWD_NW = PSA_BF16_FWD_NW, FWD_QB = W ? 2 : PSA_BF16_FWD_QB, FWD_BN = W ? 64 : PSA_BF16_FWD_BN;
+  // Forward at dk = 64: 4 waves of 48 queries held to three waves per SIMD
+  // (172 registers otherwise) reuse each K/V fragment 1.5x as often as 8
+  // waves of 32 (427-429 vs 440-441 us at N = 6400); at dk = 32 the 8-wave
+  // tiles stay (67-69 vs 59 us at N = 1600).
+  static constexpr bool F48 = !W && DK > 32 && PSA_FWD_DK64_48;
+  static constexpr int FWD_NW = F48 ? 4 : PSA_BF16_FWD_NW, FWD_QB = W ? 2 : (F48 ? 3 : PSA_BF16_FWD_QB),
+                       FWD_BN = W ? 64 : PSA_BF16_FWD_BN, FWD_OCC = F48 ? 3 : 0;
   static constexpr int BWD_NW = PSA_BF16_BWD_NW;
   // dk = 32: 32-query dK/dV tiles bring the kernel to about 162 registers,
   // three waves per SIMD (measured 5% faster at N = 1600); dk = 64 stays at
@@ -107,7 +116,7 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && DKDV_KB <= 2;
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
-  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32;
+  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32, FWD_OCC = 0;
   static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = 32;
@@ -118,7 +127,7 @@ template <int DK, int DV> struct TilesWide<float, DK, DV> {
 // faster than 64-query tiles at two workgroups per CU, at N = 400).
 template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
-  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64;
+  static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 64, FWD_OCC = 0;
   static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = W ? 32 : 64;
@@ -239,10 +248,10 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, ps
   const dim3 g((unsigned)grid), b(C::FWD_NW * 64);
   TimedLaunch tl(K_FWD, st);
   if (vec_ok<T>(N))
-    hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true>), g, b, 0, st,
+    hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true, C::FWD_OCC>), g, b, 0, st,
                        (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   else
-    hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, false>), g, b, 0, st,
+    hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, false, C::FWD_OCC>), g, b, 0, st,
                        (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   return check_launch("psa_attn_fwd launch");
 }

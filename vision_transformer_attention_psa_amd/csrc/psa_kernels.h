@@ -69,11 +69,11 @@ struct PackView {
 };
 
 // =================================================================== forward
-template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
-__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o,
-                                                         float* __restrict__ lse, int N, int n_qtiles,
-                                                         int n_blocks, float c /* scale * log2(e) */,
-                                                         const PackView pv) {
+// OCC > 0: the register allocator is held to OCC waves per SIMD.
+template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK, int OCC = 0>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1, OCC > 0 ? OCC : 8)))
+void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restrict__ lse, int N, int n_qtiles,
+                    int n_blocks, float c /* scale * log2(e) */, const PackView pv) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
