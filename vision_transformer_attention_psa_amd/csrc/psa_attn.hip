@@ -88,6 +88,11 @@ int fail(int code, const std::string& msg) {
 // and the streamed LDS tiles (their rows are twice as long), so that two
 // workgroups still fit one CU.
 template <int DK, int DV> constexpr bool wide_heads() { return DK + DV > 128; }
+// The dK/dV two-deep prefetch costs no registers only while one streamed
+// Q|dO tile (4-channel x 8-token blocks) needs at most half of the threads.
+template <int DK, int DV, int BMQ, int NW> constexpr bool deep_fits() {
+  return (DK + DV) / 4 * (BMQ / 8) <= NW * 32;
+}
 
 template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   static constexpr bool W = wide_heads<DK, DV>();
@@ -113,7 +118,7 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   // of each K/V fragment (measured 3% faster at N = 6400); at dk = 32 the
   // extra registers would cost a wave per SIMD.
   static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? PSA_BF16_DQ_QB : 3), DQ_BN = W ? 32 : PSA_BF16_DQ_BN;
-  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && DKDV_KB <= 2;
+  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && DKDV_KB <= 2 && deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32, FWD_OCC = 0;
@@ -131,7 +136,7 @@ template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
   static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = W ? 32 : 64;
-  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP;
+  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
 };
 template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, DK, DV> {};
 
