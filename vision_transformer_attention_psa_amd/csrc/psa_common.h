@@ -239,6 +239,20 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
         const T* p = base + (size_t)i * N + j;
         if constexpr (VECOK) {
           if (j < N) r[u][i] = *(const u32x4*)p;
+        } else if ((N & 3) == 0) {
+          // N a multiple of 4: rows start 8-byte aligned (j is a multiple of
+          // 8), four tokens per load; j + 4e < N implies j + 4e + 3 < N.
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const u32x2 v = (j + 4 * e < N) ? ((const u32x2*)p)[e] : u32x2{0u, 0u};
+            r[u][i][2 * e] = v[0];
+            r[u][i][2 * e + 1] = v[1];
+          }
+        } else if ((N & 1) == 0) {
+          // Even N: rows start 4-byte aligned, token pairs load as one dword;
+          // j + 2e < N implies j + 2e + 1 < N.
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[u][i][e] = (j + 2 * e < N) ? ((const unsigned*)p)[e] : 0u;
         } else {
           unsigned short tmp[8];
 #pragma unroll
