@@ -223,8 +223,13 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
                     NAT_HI % 4 == 0, "tile shape");
   u32x4 r[PER][4];
 
-  __device__ __forceinline__ void load(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0,
-                                       int tid) {
+  // One 16-byte chunk (8 tokens of one row) per (u, i); W bytes per load:
+  // 16 when N is a multiple of 8 (VECOK), else 8, 4 or 2 as the rows'
+  // alignment allows (masked per load; a load at token j + k*W/2 < N holds
+  // only tokens below N, as N is a multiple of W/2).
+  template <int W>
+  __device__ __forceinline__ void load_w(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0, int tid) {
+    constexpr int TPL = W / 2;  // tokens per load
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
@@ -237,22 +242,18 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
         r[u][i] = u32x4{0u, 0u, 0u, 0u};
         if (!live) continue;
         const T* p = base + (size_t)i * N + j;
-        if constexpr (VECOK) {
+        if constexpr (W == 16) {
           if (j < N) r[u][i] = *(const u32x4*)p;
-        } else if ((N & 3) == 0) {
-          // N a multiple of 4: rows start 8-byte aligned (j is a multiple of
-          // 8), four tokens per load; j + 4e < N implies j + 4e + 3 < N.
+        } else if constexpr (W == 8) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const u32x2 v = (j + 4 * e < N) ? ((const u32x2*)p)[e] : u32x2{0u, 0u};
+            const u32x2 v = (j + TPL * e < N) ? ((const u32x2*)p)[e] : u32x2{0u, 0u};
             r[u][i][2 * e] = v[0];
             r[u][i][2 * e + 1] = v[1];
           }
-        } else if ((N & 1) == 0) {
-          // Even N: rows start 4-byte aligned, token pairs load as one dword;
-          // j + 2e < N implies j + 2e + 1 < N.
+        } else if constexpr (W == 4) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[u][i][e] = (j + 2 * e < N) ? ((const unsigned*)p)[e] : 0u;
+          for (int e = 0; e < 4; ++e) r[u][i][e] = (j + TPL * e < N) ? ((const unsigned*)p)[e] : 0u;
         } else {
           unsigned short tmp[8];
 #pragma unroll
@@ -260,6 +261,18 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
           __builtin_memcpy(&r[u][i], tmp, 16);
         }
       }
+    }
+  }
+  __device__ __forceinline__ void load(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0,
+                                       int tid) {
+    if constexpr (VECOK) {
+      load_w<16>(lo, hi, N, j0, tid);
+    } else if ((N & 3) == 0) {  // one uniform branch per call, straight-line loads inside
+      load_w<8>(lo, hi, N, j0, tid);
+    } else if ((N & 1) == 0) {
+      load_w<4>(lo, hi, N, j0, tid);
+    } else {
+      load_w<2>(lo, hi, N, j0, tid);
     }
   }
   __device__ __forceinline__ void store(T* nat, T* tm, int tid) const {
