@@ -31,7 +31,7 @@ METRIC = "PSA attn bwd TFLOP/s + µs/call (B=16,N=400 & N=6400), % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "highres_n6400_bf16"
-ALSO = ("batched_n400_bf16", "midres_n1600_bf16")
+ALSO = ("tiny_n64_f32", "nano_n400_f32", "batched_n400_bf16", "midres_n1600_bf16")  # the other four workloads
 
 
 def flops(wl) -> dict:
