@@ -49,3 +49,5 @@ def test_traffic_keeps_the_workloads_instance(tmp_path):
 def test_short_names():
     assert rs.short_name(MAIN64).startswith("bwd_main<bf16,64,64,2,64,3,64,4")
     assert rs.short_name(PRE32) == "bwd_pre<bf16,32>"
+    demangled = "void psa::psa_fwd_kernel<float, 16, 16, 1, 4, 32, true, 0>(float const*, float*, float*, int)"
+    assert rs.short_name(demangled) == "fwd<f32,16,16,1,4,32>"

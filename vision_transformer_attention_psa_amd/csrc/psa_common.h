@@ -139,6 +139,28 @@ __device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, cons
   for (int s = 0; s < 8; ++s) f.v[s] = live ? p[s * ldn] : 0.f;
 }
 
+// The fragment frag_tok reads, taken from the channel-major tile nat[ch][token]
+// (pitch ldn) with the gfx950 transpose read ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane i receives as its element e (of 4) the 16-bit value
+// at position i % 4 of the 8 bytes that lane 4e + i/4 addressed.  So lane
+// (t, g) addresses channel k0 + 8g + 4s + t/4 at the 4 consecutive tokens
+// that result lanes 4(t%4) .. 4(t%4)+3 hold, and reads s = 0, 1 give lane
+// (t, g) channels k0 + 8g .. +7 of its token.  No token-major copy is staged.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+template <int CV, bool PERM, typename T>
+__device__ __forceinline__ void frag_tr(Frag<T>& f, const T* nat, int ldn, int row0, int h, int k0) {
+  static_assert(is_16bit<T>() && CV % 32 == 0, "16-bit element type, whole 32-channel chunks");
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const int lane = lane_id(), t = lane & 15, g = lane >> 4;
+  const int tok = row0 + (PERM ? 8 * (t & 3) + 4 * h : 4 * (t & 3));
+  const T* p = nat + (k0 + 8 * g + (t >> 2)) * ldn + tok;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * ldn));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  f.v = __builtin_bit_cast(typename Vec8<T>::type, v);
+}
+
 // Rows = channels ch0 .. ch0+15, contraction over tokens tok0 + 8g .. +7.
 template <typename T>
 __device__ __forceinline__ void frag_ch(Frag<T>& f, const T* nat, int ldn, int ch0, int tok0) {
@@ -191,7 +213,12 @@ __device__ __forceinline__ void acc_to_frag(Frag<float>& f, const f32x4& a0, con
 // ------------------------------------------------------------------ staging
 // Pitches (elements): 16 bytes of padding per row keeps every row 16-byte
 // aligned and spreads the 16 rows one fragment read touches over all banks.
-template <typename T> constexpr int nat_pitch(int tokens) { return tokens + 16 / (int)sizeof(T); }
+#ifndef PSA_NAT_PAD16
+#define PSA_NAT_PAD16 8
+#endif
+template <typename T> constexpr int nat_pitch(int tokens) {
+  return tokens + (sizeof(T) == 2 ? PSA_NAT_PAD16 : 16 / (int)sizeof(T));
+}
 constexpr int tm_pitch(int channels) { return channels + 8; }
 
 // Global -> registers -> LDS for a tile of C channel rows x BT tokens from

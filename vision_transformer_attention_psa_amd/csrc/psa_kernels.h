@@ -50,6 +50,16 @@ constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before a re
 #define PSA_OCCUPANCY
 #endif
 
+// 16-bit streamed tiles are staged channel-major only, and the contractions
+// over channels read them with the transpose read (frag_tr).  Bit mask of the
+// bodies that do so: 1 dK/dV, 2 dQ, 4 forward (the dQ body measured slower
+// with them: its staging transposes fewer rows per fragment read).
+#ifndef PSA_TR_READS
+#define PSA_TR_READS 5
+#endif
+constexpr int kTrDkdv = 1, kTrDq = 2, kTrFwd = 4;
+template <typename T, int BODY> constexpr bool tr_reads() { return (PSA_TR_READS & BODY) && is_16bit<T>(); }
+
 template <int D> struct Chunks {
   static constexpr int n = (D + 31) / 32;  // 32-wide contraction chunks
   static_assert(D % 16 == 0, "head dims must be multiples of 16");
@@ -77,13 +87,15 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
-  // K|V tile: K rows token-major (bf16) for S^T, V rows channel-major for PV.
-  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, DK, DK, DK + DV>;
+  // K|V tile: K rows token-major (16-bit) for S^T, V rows channel-major for
+  // PV; with transpose reads, K rows channel-major too.
+  constexpr bool TR = tr_reads<T, kTrFwd>();
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, TR ? 0 : DK, TR ? 0 : DK, DK + DV>;
   using SQ = Stager<T, DK, BM, NT, VECOK, DK, DK, 0, 0>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   constexpr int QE = SQ::NAT_ELEMS + SQ::TM_ELEMS;
   constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
-  constexpr int VROW = is_16bit<T>() ? 0 : DK;  // first V row in the channel-major tile
+  constexpr int VROW = is_16bit<T>() && !TR ? 0 : DK;  // first V row in the channel-major tile
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -146,7 +158,10 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          if constexpr (TR)
+            frag_tr<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          else
+            frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
@@ -308,8 +323,10 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
 template <typename T, int DK, int DV, int KB, int NW, int BMQ>
 struct DkdvShape {
   static constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
-  // Q|dO tile: both layouts of every row.  K|V stationary tile: token-major.
-  using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, DK + DV, 0, DK + DV>;
+  // Q|dO tile: channel-major (and token-major without transpose reads).
+  // K|V stationary tile: token-major.
+  static constexpr int QG_TM = tr_reads<T, kTrDkdv>() ? 0 : DK + DV;
+  using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, QG_TM, 0, DK + DV>;
   using SKV = Stager<T, DK + DV, BNK, NT, true, DK, DK + DV, 0, 0>;
   static constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 4 * BMQ * (int)sizeof(float);
@@ -329,9 +346,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BMQ % 32 == 0, "query tile must be a multiple of 32");
   static_assert(BMQ <= NT, "one statistics entry per thread");
-  using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, DK + DV, 0, DK + DV>;
+  constexpr bool TR = tr_reads<T, kTrDkdv>();
+  using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, Shape::QG_TM, 0, DK + DV>;
   using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK, DK + DV, 0, 0>;
   constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  static_assert(TILE == Shape::TILE, "tile layout");
   T* smem = (T*)smem_raw;
   float* snl = (float*)(smem_raw + 2 * TILE * sizeof(T));  // [2][BMQ], then snd [2][BMQ]
   float* snd = snl + 2 * BMQ;
@@ -388,7 +407,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // in its registers from the top of iteration qt to the end of qt + 1: a
   // prefetch distance of two tiles, at the register cost of one wherever a
   // tile needs no more than half the threads.
-  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK, DK + DV, 0, DK + DV>;
+  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK, Shape::QG_TM, 0, DK + DV>;
   static_assert(!DEEP || BMQ <= NT / 2, "one statistics entry per thread of a half");
   const int half = tid >= NT / 2, htid = tid - half * (NT / 2);
   SQH sh;
@@ -444,14 +463,20 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          frag_tok<DK, true>(a, tm, SQG::LDT, nat, SQG::LDN, 32 * c2, h, 32 * kc);
+          if constexpr (TR)
+            frag_tr<DK, true>(a, nat, SQG::LDN, 32 * c2, h, 32 * kc);
+          else
+            frag_tok<DK, true>(a, tm, SQG::LDT, nat, SQG::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(s[h][kb], a, kf[kb][kc]);
         }
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
           Frag<T> a;
-          frag_tok<DV, true>(a, tm + DK, SQG::LDT, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
+          if constexpr (TR)
+            frag_tr<DV, true>(a, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
+          else
+            frag_tok<DV, true>(a, tm + DK, SQG::LDT, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(dp[h][kb], a, vf[kb][cc]);
         }
@@ -535,8 +560,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 template <typename T, int DK, int DV, int QB, int NW, int BN>
 struct DqShape {
   static constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
-  // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T).
-  using SKV = Stager<T, DK + DV, BN, NT, true, DK, DK + DV, 0, DK>;
+  // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T);
+  // with transpose reads, K and V rows channel-major only.
+  static constexpr bool TR = tr_reads<T, kTrDq>();
+  static constexpr int KV_TM = TR ? 0 : DK + DV, KV_NAT = TR ? DK + DV : DK;
+  using SKV = Stager<T, DK + DV, BN, NT, true, DK, KV_TM, 0, KV_NAT>;
   // Stationary Q|dO tile, token-major.
   using SQG = Stager<T, DK + DV, BM, NT, true, DK, DK + DV, 0, 0>;
   static constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
@@ -553,9 +581,11 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   constexpr int QW = Shape::QW, BM = Shape::BM, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
-  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, DK + DV, 0, DK>;
+  constexpr bool TR = Shape::TR;
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, Shape::KV_TM, 0, Shape::KV_NAT>;
   using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, DK + DV, 0, 0>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
+  static_assert(BUF == Shape::BUF, "tile layout");
   T* smem = (T*)smem_raw;
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -604,8 +634,8 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
-    const T* nat = smem + (kt & 1) * BUF;  // K channel-major (fp32: K then V)
-    const T* tm = tm_of(nat, sk);          // K then V channels, token-major
+    const T* nat = smem + (kt & 1) * BUF;  // K channel-major (fp32, TR: K then V)
+    const T* tm = tm_of(nat, sk);          // K then V channels, token-major (not TR)
     if (kt + 1 < nkt) sk.load(KVg, Vg, N, (kt + 1) * BN, tid);
 
 #pragma unroll
@@ -622,14 +652,20 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          if constexpr (TR)
+            frag_tr<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          else
+            frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
           Frag<T> a;
-          frag_tok<DV, true>(a, tm + DK, SKV::LDT, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
+          if constexpr (TR)
+            frag_tr<DV, true>(a, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
+          else
+            frag_tok<DV, true>(a, tm + DK, SKV::LDT, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }

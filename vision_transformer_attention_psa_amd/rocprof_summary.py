@@ -43,6 +43,12 @@ def short_name(kernel: str) -> str:
                 dt = {"DF16b": "bf16", "DF16_": "f16"}.get(m.group(1), "f32")
                 dims = re.findall(r"Li(\d+)E", m.group(2))
                 return f"{slot}<{','.join([dt] + dims)}>"
+            # fully demangled (fp32 instances): psa_fwd_kernel<float, 16, 16, ...>
+            m = re.search(pat + r"<(float|__bf16|_Float16)((?:, \d+)*)", kernel)
+            if m:
+                dt = {"__bf16": "bf16", "_Float16": "f16"}.get(m.group(1), "f32")
+                dims = re.findall(r"\d+", m.group(2))
+                return f"{slot}<{','.join([dt] + dims)}>"
             return slot
     return kernel[:60]
 
