@@ -143,22 +143,39 @@ __device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, cons
 // (pitch ldn) with the gfx950 transpose read ds_read_b64_tr_b16: within each
 // group of 16 lanes, lane i receives as its element e (of 4) the 16-bit value
 // at position i % 4 of the 8 bytes that lane 4e + i/4 addressed.  So lane
-// (t, g) addresses channel k0 + 8g + 4s + t/4 at the 4 consecutive tokens
-// that result lanes 4(t%4) .. 4(t%4)+3 hold, and reads s = 0, 1 give lane
-// (t, g) channels k0 + 8g .. +7 of its token.  No token-major copy is staged.
+// (t, g) addresses one channel row at the 4 consecutive tokens that result
+// lanes 4(t%4) .. 4(t%4)+3 hold, and two reads give lane (t, g) eight channels
+// of its token.
+// PSA_TR_ILV (default): the first read takes channels k0 + 8g + {0, 1, 4, 5},
+// the second {2, 3, 6, 7}, so that the four rows one read touches are spread
+// over the banks (consecutive rows, 16 bytes apart within each row, meet at
+// the same banks); the fragment then holds its channels in the order
+// 0 1 4 5 2 3 6 7, and the other MFMA operand is put in that order once with
+// tr_order().  Otherwise the reads take {0..3} and {4..7}, in natural order.
+#ifndef PSA_TR_ILV
+#define PSA_TR_ILV 1
+#endif
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 template <int CV, bool PERM, typename T>
 __device__ __forceinline__ void frag_tr(Frag<T>& f, const T* nat, int ldn, int row0, int h, int k0) {
   static_assert(is_16bit<T>() && CV % 32 == 0, "16-bit element type, whole 32-channel chunks");
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const int lane = lane_id(), t = lane & 15, g = lane >> 4;
+  const int lane = lane_id(), t = lane & 15, g = lane >> 4, e = t >> 2;
   const int tok = row0 + (PERM ? 8 * (t & 3) + 4 * h : 4 * (t & 3));
-  const T* p = nat + (k0 + 8 * g + (t >> 2)) * ldn + tok;
+  const int ch = k0 + 8 * g + (PSA_TR_ILV ? (e & 1) + 4 * (e >> 1) : e);
+  const T* p = nat + ch * ldn + tok;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * ldn));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (PSA_TR_ILV ? 2 : 4) * ldn));
   const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   f.v = __builtin_bit_cast(typename Vec8<T>::type, v);
+}
+// A fragment in natural channel order -> the order frag_tr produces.
+template <typename T> __device__ __forceinline__ void tr_order(Frag<T>& f) {
+  if constexpr (PSA_TR_ILV) {
+    const u32x4 d = __builtin_bit_cast(u32x4, f.v);
+    f.v = __builtin_bit_cast(typename Vec8<T>::type, u32x4{d[0], d[2], d[1], d[3]});
+  }
 }
 
 // Rows = channels ch0 .. ch0+15, contraction over tokens tok0 + 8g .. +7.

@@ -115,8 +115,10 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
 #pragma unroll
     for (int nb = 0; nb < QB; ++nb)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
+      for (int kc = 0; kc < KC; ++kc) {
         frag_tok<DK, false>(qf[nb][kc], tm_of(smem, sq), SQ::LDT, smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
+        if constexpr (TR) tr_order(qf[nb][kc]);  // K fragments come from frag_tr
+      }
     __syncthreads();
   }
 
@@ -377,10 +379,15 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
     for (int kb = 0; kb < KB; ++kb) {
       const int row0 = w * KW + 16 * kb;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) frag_tok<DK, false>(kf[kb][kc], tm, SKV::LDT, smem, SKV::LDN, row0, 0, 32 * kc);
+      for (int kc = 0; kc < KC; ++kc) {
+        frag_tok<DK, false>(kf[kb][kc], tm, SKV::LDT, smem, SKV::LDN, row0, 0, 32 * kc);
+        if constexpr (TR) tr_order(kf[kb][kc]);  // Q fragments come from frag_tr
+      }
 #pragma unroll
-      for (int cc = 0; cc < CC; ++cc)
+      for (int cc = 0; cc < CC; ++cc) {
         frag_tok<DV, false>(vf[kb][cc], tm + DK, SKV::LDT, smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
+        if constexpr (TR) tr_order(vf[kb][cc]);  // dO fragments come from frag_tr
+      }
     }
     __syncthreads();
   }
