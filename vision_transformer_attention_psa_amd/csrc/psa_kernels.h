@@ -52,10 +52,9 @@ constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before a re
 
 // 16-bit streamed tiles are staged channel-major only, and the contractions
 // over channels read them with the transpose read (frag_tr).  Bit mask of the
-// bodies that do so: 1 dK/dV, 2 dQ, 4 forward (the dQ body measured slower
-// with them: its staging transposes fewer rows per fragment read).
+// bodies that do so: 1 dK/dV, 2 dQ, 4 forward.
 #ifndef PSA_TR_READS
-#define PSA_TR_READS 5
+#define PSA_TR_READS 7
 #endif
 constexpr int kTrDkdv = 1, kTrDq = 2, kTrFwd = 4;
 template <typename T, int BODY> constexpr bool tr_reads() { return (PSA_TR_READS & BODY) && is_16bit<T>(); }
@@ -617,10 +616,15 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
     for (int nb = 0; nb < QB; ++nb) {
       const int row0 = w * QW + 16 * nb;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) frag_tok<DK, false>(qf[nb][kc], tm, SQG::LDT, smem, SQG::LDN, row0, 0, 32 * kc);
+      for (int kc = 0; kc < KC; ++kc) {
+        frag_tok<DK, false>(qf[nb][kc], tm, SQG::LDT, smem, SQG::LDN, row0, 0, 32 * kc);
+        if constexpr (TR) tr_order(qf[nb][kc]);  // K fragments come from frag_tr
+      }
 #pragma unroll
-      for (int cc = 0; cc < CC; ++cc)
+      for (int cc = 0; cc < CC; ++cc) {
         frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
+        if constexpr (TR) tr_order(gf[nb][cc]);  // V fragments come from frag_tr
+      }
       const int i = i0 + row0 + t;
       nl[nb] = i < N ? nlg[(size_t)bh * N + i] : kNegInf;
       nd[nb] = i < N ? ndg[(size_t)bh * N + i] : 0.f;
