@@ -150,8 +150,8 @@ __device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, cons
 // the second {2, 3, 6, 7}, so that the four rows one read touches are spread
 // over the banks (consecutive rows, 16 bytes apart within each row, meet at
 // the same banks); the fragment then holds its channels in the order
-// 0 1 4 5 2 3 6 7, and the other MFMA operand is put in that order once with
-// tr_order().  Otherwise the reads take {0..3} and {4..7}, in natural order.
+// 0 1 4 5 2 3 6 7, which is harmless as long as the other MFMA operand is
+// read with frag_tr as well.  Otherwise the reads take {0..3} and {4..7}.
 #ifndef PSA_TR_ILV
 #define PSA_TR_ILV 1
 #endif
@@ -169,13 +169,6 @@ __device__ __forceinline__ void frag_tr(Frag<T>& f, const T* nat, int ldn, int r
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (PSA_TR_ILV ? 2 : 4) * ldn));
   const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   f.v = __builtin_bit_cast(typename Vec8<T>::type, v);
-}
-// A fragment in natural channel order -> the order frag_tr produces.
-template <typename T> __device__ __forceinline__ void tr_order(Frag<T>& f) {
-  if constexpr (PSA_TR_ILV) {
-    const u32x4 d = __builtin_bit_cast(u32x4, f.v);
-    f.v = __builtin_bit_cast(typename Vec8<T>::type, u32x4{d[0], d[2], d[1], d[3]});
-  }
 }
 
 // Rows = channels ch0 .. ch0+15, contraction over tokens tok0 + 8g .. +7.

@@ -90,7 +90,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   // PV; with transpose reads, K rows channel-major too.
   constexpr bool TR = tr_reads<T, kTrFwd>();
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, TR ? 0 : DK, TR ? 0 : DK, DK + DV>;
-  using SQ = Stager<T, DK, BM, NT, VECOK, DK, DK, 0, 0>;
+  using SQ = Stager<T, DK, BM, NT, VECOK, DK, TR ? 0 : DK, 0, TR ? DK : 0>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   constexpr int QE = SQ::NAT_ELEMS + SQ::TM_ELEMS;
   constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
@@ -115,8 +115,10 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
     for (int nb = 0; nb < QB; ++nb)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        frag_tok<DK, false>(qf[nb][kc], tm_of(smem, sq), SQ::LDT, smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
-        if constexpr (TR) tr_order(qf[nb][kc]);  // K fragments come from frag_tr
+        if constexpr (TR)
+          frag_tr<DK, false>(qf[nb][kc], smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
+        else
+          frag_tok<DK, false>(qf[nb][kc], tm_of(smem, sq), SQ::LDT, smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
       }
     __syncthreads();
   }
@@ -327,8 +329,9 @@ struct DkdvShape {
   // Q|dO tile: channel-major (and token-major without transpose reads).
   // K|V stationary tile: token-major.
   static constexpr int QG_TM = tr_reads<T, kTrDkdv>() ? 0 : DK + DV;
+  static constexpr int KV_TM = QG_TM, KV_NAT = DK + DV - QG_TM;
   using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, QG_TM, 0, DK + DV>;
-  using SKV = Stager<T, DK + DV, BNK, NT, true, DK, DK + DV, 0, 0>;
+  using SKV = Stager<T, DK + DV, BNK, NT, true, DK, KV_TM, 0, KV_NAT>;
   static constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 4 * BMQ * (int)sizeof(float);
   static_assert(2 * TILE * sizeof(T) % 16 == 0, "statistics must be 16-byte aligned");
@@ -349,7 +352,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   static_assert(BMQ <= NT, "one statistics entry per thread");
   constexpr bool TR = tr_reads<T, kTrDkdv>();
   using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, Shape::QG_TM, 0, DK + DV>;
-  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK, DK + DV, 0, 0>;
+  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK, Shape::KV_TM, 0, Shape::KV_NAT>;
   constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   static_assert(TILE == Shape::TILE, "tile layout");
   T* smem = (T*)smem_raw;
@@ -379,13 +382,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
       const int row0 = w * KW + 16 * kb;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        frag_tok<DK, false>(kf[kb][kc], tm, SKV::LDT, smem, SKV::LDN, row0, 0, 32 * kc);
-        if constexpr (TR) tr_order(kf[kb][kc]);  // Q fragments come from frag_tr
+        if constexpr (TR)
+          frag_tr<DK, false>(kf[kb][kc], smem, SKV::LDN, row0, 0, 32 * kc);
+        else
+          frag_tok<DK, false>(kf[kb][kc], tm, SKV::LDT, smem, SKV::LDN, row0, 0, 32 * kc);
       }
 #pragma unroll
       for (int cc = 0; cc < CC; ++cc) {
-        frag_tok<DV, false>(vf[kb][cc], tm + DK, SKV::LDT, smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
-        if constexpr (TR) tr_order(vf[kb][cc]);  // dO fragments come from frag_tr
+        if constexpr (TR)
+          frag_tr<DV, false>(vf[kb][cc], smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
+        else
+          frag_tok<DV, false>(vf[kb][cc], tm + DK, SKV::LDT, smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
       }
     }
     __syncthreads();
@@ -571,8 +578,9 @@ struct DqShape {
   static constexpr bool TR = tr_reads<T, kTrDq>();
   static constexpr int KV_TM = TR ? 0 : DK + DV, KV_NAT = TR ? DK + DV : DK;
   using SKV = Stager<T, DK + DV, BN, NT, true, DK, KV_TM, 0, KV_NAT>;
-  // Stationary Q|dO tile, token-major.
-  using SQG = Stager<T, DK + DV, BM, NT, true, DK, DK + DV, 0, 0>;
+  // Stationary Q|dO tile, token-major (channel-major with transpose reads).
+  static constexpr int QG_TM = TR ? 0 : DK + DV, QG_NAT = TR ? DK + DV : 0;
+  using SQG = Stager<T, DK + DV, BM, NT, true, DK, QG_TM, 0, QG_NAT>;
   static constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   static constexpr int QE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
   static constexpr int SMEM = (2 * BUF > QE ? 2 * BUF : QE) * (int)sizeof(T);
@@ -589,7 +597,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
   constexpr bool TR = Shape::TR;
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, Shape::KV_TM, 0, Shape::KV_NAT>;
-  using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, DK + DV, 0, 0>;
+  using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, Shape::QG_TM, 0, Shape::QG_NAT>;
   constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
   static_assert(BUF == Shape::BUF, "tile layout");
   T* smem = (T*)smem_raw;
@@ -617,13 +625,17 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
       const int row0 = w * QW + 16 * nb;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        frag_tok<DK, false>(qf[nb][kc], tm, SQG::LDT, smem, SQG::LDN, row0, 0, 32 * kc);
-        if constexpr (TR) tr_order(qf[nb][kc]);  // K fragments come from frag_tr
+        if constexpr (TR)
+          frag_tr<DK, false>(qf[nb][kc], smem, SQG::LDN, row0, 0, 32 * kc);
+        else
+          frag_tok<DK, false>(qf[nb][kc], tm, SQG::LDT, smem, SQG::LDN, row0, 0, 32 * kc);
       }
 #pragma unroll
       for (int cc = 0; cc < CC; ++cc) {
-        frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
-        if constexpr (TR) tr_order(gf[nb][cc]);  // V fragments come from frag_tr
+        if constexpr (TR)
+          frag_tr<DV, false>(gf[nb][cc], smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
+        else
+          frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
       }
       const int i = i0 + row0 + t;
       nl[nb] = i < N ? nlg[(size_t)bh * N + i] : kNegInf;
