@@ -155,6 +155,14 @@ __device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, cons
 #ifndef PSA_TR_ILV
 #define PSA_TR_ILV 1
 #endif
+// 16-bit tiles are staged channel-major only, and the contractions over
+// channels read them with frag_tr.  Bit mask of the kernels that do so:
+// 1 dK/dV body, 2 dQ body, 4 forward, 8 convolution dx.
+#ifndef PSA_TR_READS
+#define PSA_TR_READS 15
+#endif
+constexpr int kTrDkdv = 1, kTrDq = 2, kTrFwd = 4, kTrConvDx = 8;
+template <typename T, int BODY> constexpr bool tr_reads() { return (PSA_TR_READS & BODY) && is_16bit<T>(); }
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 template <int CV, bool PERM, typename T>

@@ -12,9 +12,9 @@
 //
 // Both GEMMs run on MFMA with 4 waves per workgroup, each owning a 64 x 64
 // output tile (2 x 2 waves: 128 x 128 per workgroup).
-//   dx: contraction over co, which is the slow index of both w and dy, so
-//       both operands are staged token-major (rows ci resp. n, co
-//       contiguous) and read with frag_tok.
+//   dx: contraction over co, which is the slow index of both w and dy: both
+//       tiles are staged channel-major (rows co) and read with the transpose
+//       read (frag_tr), or staged token-major and read with frag_tok.
 //   dw: contraction over n, the fast index of both dy and x: both tiles are
 //       channel-major and read with frag_ch, as the attention's dV/dK GEMMs.
 #pragma once
@@ -53,9 +53,12 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
                                                           int n_ntiles, int n_citiles, int n_blocks) {
   constexpr int KCH = is_16bit<T>() ? 64 : 32, BT = kConvTile, NT = 256;  // fp32 tiles are twice as wide
   constexpr int KC = KCH / 32;
-  // rows = co (channels of the chunk), tokens = ci (w) or n (dy)
-  using SW = Stager<T, KCH, BT, NT, true, KCH, (is_16bit<T>() ? KCH : 0), 0, (is_16bit<T>() ? 0 : KCH)>;
-  using SY = Stager<T, KCH, BT, NT, VECOK, KCH, (is_16bit<T>() ? KCH : 0), 0, (is_16bit<T>() ? 0 : KCH)>;
+  // rows = co (channels of the chunk), tokens = ci (w) or n (dy); with
+  // transpose reads both tiles stay channel-major and frag_tr reads them.
+  constexpr bool TR = tr_reads<T, kTrConvDx>();
+  constexpr int TMR = is_16bit<T>() && !TR ? KCH : 0, NATR = KCH - TMR;
+  using SW = Stager<T, KCH, BT, NT, true, KCH, TMR, 0, NATR>;
+  using SY = Stager<T, KCH, BT, NT, VECOK, KCH, TMR, 0, NATR>;
   constexpr int BUF = SW::NAT_ELEMS + SW::TM_ELEMS;  // one operand tile
   __shared__ __attribute__((aligned(16))) T smem[4 * BUF];
 
@@ -101,11 +104,19 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
     for (int kc = 0; kc < KC; ++kc) {
       Frag<T> fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        frag_tok<KCH, false>(fa[i], a + SW::NAT_ELEMS, SW::LDT, a, SW::LDN, wr + 16 * i, 0, 32 * kc);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (TR)
+          frag_tr<KCH, false>(fa[i], a, SW::LDN, wr + 16 * i, 0, 32 * kc);
+        else
+          frag_tok<KCH, false>(fa[i], a + SW::NAT_ELEMS, SW::LDT, a, SW::LDN, wr + 16 * i, 0, 32 * kc);
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        frag_tok<KCH, false>(fb[j], y + SY::NAT_ELEMS, SY::LDT, y, SY::LDN, wc + 16 * j, 0, 32 * kc);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (TR)
+          frag_tr<KCH, false>(fb[j], y, SY::LDN, wc + 16 * j, 0, 32 * kc);
+        else
+          frag_tok<KCH, false>(fb[j], y + SY::NAT_ELEMS, SY::LDT, y, SY::LDN, wc + 16 * j, 0, 32 * kc);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -50,14 +50,6 @@ constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before a re
 #define PSA_OCCUPANCY
 #endif
 
-// 16-bit streamed tiles are staged channel-major only, and the contractions
-// over channels read them with the transpose read (frag_tr).  Bit mask of the
-// bodies that do so: 1 dK/dV, 2 dQ, 4 forward.
-#ifndef PSA_TR_READS
-#define PSA_TR_READS 7
-#endif
-constexpr int kTrDkdv = 1, kTrDq = 2, kTrFwd = 4;
-template <typename T, int BODY> constexpr bool tr_reads() { return (PSA_TR_READS & BODY) && is_16bit<T>(); }
 
 template <int D> struct Chunks {
   static constexpr int n = (D + 31) / 32;  // 32-wide contraction chunks
