@@ -65,6 +65,9 @@ int fail(int code, const std::string& msg) {
 #ifndef PSA_BF16_DQ_BN
 #define PSA_BF16_DQ_BN 64
 #endif
+#ifndef PSA_BF16_DQ_BN_DK64
+#define PSA_BF16_DQ_BN_DK64 128
+#endif
 // dK/dV body: query tiles prefetched two iterations ahead (the thread halves
 // take turns).  Measured -4% at N = 400, -3% at N = 1600, -0.7% at N = 6400;
 // the same for the dQ body's and the forward's key tiles measured no gain.
@@ -116,8 +119,11 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   // dk = 64: 48 queries per dQ wave fit within the registers the dK/dV body
   // already needs, so the launch keeps two waves per SIMD with 1.5x the reuse
   // of each K/V fragment (measured 3% faster at N = 6400); at dk = 32 the
-  // extra registers would cost a wave per SIMD.
-  static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? PSA_BF16_DQ_QB : 3), DQ_BN = W ? 32 : PSA_BF16_DQ_BN;
+  // extra registers would cost a wave per SIMD.  dk = 64: 128-key dQ tiles
+  // (half the barriers per key; same registers, 70 KB of LDS) measured
+  // 1044 vs 1059 us at N = 6400; at dk = 32 they cost 2-6%.
+  static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? PSA_BF16_DQ_QB : 3),
+                       DQ_BN = W ? 32 : (DK <= 32 ? PSA_BF16_DQ_BN : PSA_BF16_DQ_BN_DK64);
   static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && DKDV_KB <= 2 && deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
