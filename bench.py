@@ -17,9 +17,11 @@ inputs.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -29,7 +31,10 @@ if ROOT not in sys.path:
 
 METRIC = "PSA attn bwd TFLOP/s + µs/call (B=16,N=400 & N=6400), % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+# dense MFMA flops per clock per CU: 2516.6 TFLOP/s = 256 CUs x 2.4 GHz x 4096
+FLOP_PER_CLK_CU = {"bf16": 4096, "f16": 4096, "f32": 256}
 PEAK_HBM_GBS = 8000.0
+BATCHES = 5  # per-call times are the median over this many batches of K calls
 HEADLINE = "highres_n6400_bf16"
 ALSO = ("tiny_n64_f32", "nano_n400_f32", "batched_n400_bf16", "midres_n1600_bf16")  # the other four workloads
 
@@ -108,10 +113,38 @@ def device_inputs(torch, x):
     return q, g
 
 
+def device_peak(dtype: str) -> dict | None:
+    """The dense MFMA peak recomputed from the device's own CU count and peak
+    clock (hipDeviceGetAttribute), next to the published figure."""
+    # the HIP runtime already in the process (torch's): loading another copy
+    # would start a second runtime on the same device
+    with open("/proc/self/maps") as f:
+        paths = {ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln}
+    if not paths:
+        return None
+    try:
+        hip = ctypes.CDLL(sorted(paths)[0])
+        val = ctypes.c_int()
+        dev = ctypes.c_int()
+        if hip.hipGetDevice(ctypes.byref(dev)) != 0:
+            return None
+        out = {}
+        for name, attr in (("cus", 63), ("clock_khz", 5)):  # MultiprocessorCount, ClockRate
+            if hip.hipDeviceGetAttribute(ctypes.byref(val), attr, dev) != 0:
+                return None
+            out[name] = val.value
+    except OSError:
+        return None
+    out["tflops"] = out["cus"] * out["clock_khz"] * 1e3 * FLOP_PER_CLK_CU[dtype] / 1e12
+    out["published_tflops"] = PEAK_TFLOPS[dtype]
+    return out
+
+
 def time_workload(torch, wl, steps: int, warmup: int) -> dict:
     """W untimed warm-up steps, then exactly K timed fwd+bwd steps (no library
-    instrumentation), then K fwd-only and K bwd-only calls back to back for
-    per-call times, then K instrumented steps for per-kernel device times."""
+    instrumentation), then BATCHES batches of K fwd-only and K bwd-only calls
+    back to back (per-call time: the median over the batches), then K
+    instrumented steps for per-kernel device times."""
     from vision_transformer_attention_psa_amd import binding, inputs
     x = inputs.make_inputs(wl)
     qkv, dO = device_inputs(torch, x)
@@ -129,7 +162,6 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         fwd()
         bwd()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -137,16 +169,21 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
         bwd()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ev[0].record()
-    for _ in range(steps):
-        fwd()
-    ev[1].record()
-    for _ in range(steps):
-        bwd()
-    ev[2].record()
-    torch.cuda.synchronize()
-    fwd_ms = ev[0].elapsed_time(ev[1]) / steps
-    bwd_ms = ev[1].elapsed_time(ev[2]) / steps
+    fwd_b, bwd_b = [], []
+    for _ in range(BATCHES):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for _ in range(steps):
+            fwd()
+        ev[1].record()
+        for _ in range(steps):
+            bwd()
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd_b.append(ev[0].elapsed_time(ev[1]) / steps)
+        bwd_b.append(ev[1].elapsed_time(ev[2]) / steps)
+    fwd_ms = statistics.median(fwd_b)
+    bwd_ms = statistics.median(bwd_b)
     binding.psa_attn_timing_reset()
     binding.psa_attn_timing_enable(True)
     for _ in range(steps):
@@ -159,11 +196,18 @@ def time_workload(torch, wl, steps: int, warmup: int) -> dict:
     fl = flops(wl)
     dt = wl.dtype
     peak = PEAK_TFLOPS[dt]
+    by = hbm_bytes(wl, 4 if dt == inputs.F32 else 2)
     avg = {k: (ms / n if n else float("nan")) for k, (ms, n) in kern.items()}
     return {
+        "inputs": x,
         "ms_per_step": (t1 - t0) * 1e3 / steps,
         "fwd_us": fwd_ms * 1e3,
         "bwd_us": bwd_ms * 1e3,
+        "batch_us": {"fwd": [v * 1e3 for v in fwd_b], "bwd": [v * 1e3 for v in bwd_b]},
+        "fwd_GBps": by["fwd"] / (fwd_ms * 1e-3) / 1e9,
+        "bwd_GBps": by["bwd"] / (bwd_ms * 1e-3) / 1e9,
+        "fwd_frac_hbm_peak": by["fwd"] / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "bwd_frac_hbm_peak": by["bwd"] / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "fwd_tflops": fl["fwd"] / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": fl["bwd"] / (bwd_ms * 1e-3) / 1e12,
         "fwd_bwd_tflops": (fl["fwd"] + fl["bwd"]) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12,
@@ -424,37 +468,61 @@ def roofline(wl, r: dict, traffic: dict | None) -> dict:
             "traffic_unit": "bytes/launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"}
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
-    """The float64 oracle on whole (b,h) slices of the same workload until
-    about `budget_s` seconds of CPU work have run (at least one slice)."""
-    from oracle import psa_oracle as orc
-    from vision_transformer_attention_psa_amd import inputs
+def _oracle_threads() -> tuple[int, int]:
+    """(threads the oracle's BLAS actually runs, host cores this process may
+    use).  The BLAS pool is sized by the environment (OMP_NUM_THREADS); it
+    cannot run more threads at once than the cores the process may use."""
+    host = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
-    one = wl.with_(B=1, heads=1)
-    fl = flops(one)
+        blas = 1
+    return min(blas, host), host
+
+
+def _time_oracle(wl, x, budget_s: float) -> dict:
+    """The float64 oracle on whole (b,h) slices of the draw x (the very
+    inputs the GPU was timed on), in slice order, until about budget_s
+    seconds of work have run (at least one slice)."""
+    from oracle import psa_oracle as orc
+    fl = flops(wl.with_(B=1, heads=1))
     fwd_s = bwd_s = 0.0
     n = 0
     while n < wl.BH and (n == 0 or fwd_s + bwd_s < budget_s):
-        x = inputs.make_inputs(one, seed=wl.seed * 1000 + n)
+        b, h = divmod(n, wl.heads)
+        q = x.qkv[b:b + 1, h:h + 1]
+        g = x.dO[b:b + 1, h:h + 1]
         t0 = time.perf_counter()
-        o, lse = orc.forward(x.qkv, one.dk, one.dv, one.scale)
+        o, lse = orc.forward(q, wl.dk, wl.dv, wl.scale)
         t1 = time.perf_counter()
-        orc.backward(x.qkv, o, lse, x.dO, one.dk, one.dv, one.scale)
+        orc.backward(q, o, lse, g, wl.dk, wl.dv, wl.scale)
         t2 = time.perf_counter()
         fwd_s += t1 - t0
         bwd_s += t2 - t1
         n += 1
-    return {"value": fl["bwd"] * n / bwd_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+    return {"slices": n, "of": wl.BH, "fwd_ms_per_slice": fwd_s / n * 1e3, "bwd_ms_per_slice": bwd_s / n * 1e3,
+            "bwd_tflops": fl["bwd"] * n / bwd_s / 1e12,
+            "fwd_us_per_call": fwd_s / n * wl.BH * 1e6, "bwd_us_per_call": bwd_s / n * wl.BH * 1e6}
+
+
+def cpu_baseline(wl, x, budget_s: float, others: dict) -> dict:
+    """The oracle as it stands, on the host, on the same seeded inputs the
+    GPU timed: the headline workload for about budget_s seconds, and each
+    other workload in `others` ({name: (workload, inputs)}) for a few
+    seconds at most."""
+    used, host = _oracle_threads()
+    head = _time_oracle(wl, x, budget_s)
+    per = {name: _time_oracle(w, xi, min(4.0, budget_s)) for name, (w, xi) in others.items()}
+    return {"value": head["bwd_tflops"], "unit": "TFLOP/s", "cores": used, "host_cores": host,
             "kind": "oracle",
-            "sample": f"{n} of {wl.BH} (b,h) slices of {wl.name} (N={wl.N}, dk={wl.dk}, "
-                      f"dv={wl.dv}), float64 numpy; bwd {bwd_s / n * 1e3:.0f} ms/slice, "
-                      f"fwd {fwd_s / n * 1e3:.0f} ms/slice; BLAS threads={threads}",
-            "bwd_us_per_call_extrapolated": bwd_s / n * wl.BH * 1e6,
-            "fwd_us_per_call_extrapolated": fwd_s / n * wl.BH * 1e6}
+            "sample": f"{head['slices']} of {wl.BH} (b,h) slices of {wl.name} (N={wl.N}, dk={wl.dk}, "
+                      f"dv={wl.dv}), the same seeded draw the GPU timed; float64 numpy, BLAS on "
+                      f"{used} threads ({host} host cores available); bwd "
+                      f"{head['bwd_ms_per_slice']:.0f} ms/slice, fwd {head['fwd_ms_per_slice']:.0f} ms/slice",
+            "bwd_us_per_call_extrapolated": head["bwd_us_per_call"],
+            "fwd_us_per_call_extrapolated": head["fwd_us_per_call"],
+            "per_workload": per}
 
 
 def main() -> int:
@@ -493,11 +561,13 @@ def main() -> int:
     r = time_workload(torch, wl, args.steps, args.warmup)
     print(f"[bench] {wl.name}: fwd {r['fwd_us']:.1f} us, bwd {r['bwd_us']:.1f} us, "
           f"bwd {r['bwd_tflops']:.1f} TFLOP/s, kernels {r['kernel_avg_us']}", file=sys.stderr, flush=True)
-    also = {}
+    also, drawn = {}, {}
     for name in [a for a in args.also.split(",") if a]:
         a = time_workload(torch, inputs.WORKLOADS[name], args.steps, args.warmup)
+        drawn[name] = (inputs.WORKLOADS[name], a["inputs"])
         also[name] = {k: a[k] for k in ("fwd_us", "bwd_us", "bwd_tflops", "bwd_pct_mfma_peak",
-                                        "fwd_bwd_tflops", "fwd_bwd_pct_mfma_peak", "kernel_avg_us")}
+                                        "fwd_bwd_tflops", "fwd_bwd_pct_mfma_peak", "fwd_GBps", "bwd_GBps",
+                                        "fwd_frac_hbm_peak", "bwd_frac_hbm_peak", "kernel_avg_us", "batch_us")}
         print(f"[bench] {name}: fwd {a['fwd_us']:.1f} us, bwd {a['bwd_us']:.1f} us, "
               f"bwd {a['bwd_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
     graph = {}
@@ -530,7 +600,7 @@ def main() -> int:
     if args.cpu_budget > 0:
         print(f"[bench] cpu baseline: oracle on {wl.name} slices (~{args.cpu_budget:.0f} s)",
               file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu = cpu_baseline(wl, r["inputs"], args.cpu_budget, drawn)
     out = {
         "metric": METRIC,
         "value": r["bwd_tflops"],
@@ -551,6 +621,12 @@ def main() -> int:
         "fwd_us_per_call": r["fwd_us"],
         "fwd_bwd_tflops": r["fwd_bwd_tflops"],
         "fwd_bwd_pct_mfma_peak": r["fwd_bwd_pct_mfma_peak"],
+        "fwd_GBps": r["fwd_GBps"],
+        "bwd_GBps": r["bwd_GBps"],
+        "fwd_frac_hbm_peak": r["fwd_frac_hbm_peak"],
+        "bwd_frac_hbm_peak": r["bwd_frac_hbm_peak"],
+        "batch_us": r["batch_us"],
+        "device_peak": device_peak(r["dtype"]),
         "kernel_avg_us": r["kernel_avg_us"],
         "roofline": roofline(wl, r, traffic),
         "cpu_baseline": cpu,

@@ -23,17 +23,26 @@
  *                                 scale included
  * Element type of qkv, o, dO and d_packed is given by `dtype`.
  *
- * Pointers are device pointers (hipMalloc'd or equivalent) that the caller
- * owns; the library never frees or retains them.  Base addresses must be
- * 16-byte aligned.  `stream` is a hipStream_t (NULL = the null stream).
+ * Pointers are device pointers (hipMalloc'd or equivalent, on the current
+ * device) that the caller owns; the library never frees or retains them.
+ * Before anything is enqueued, every pointer is looked up with the HIP
+ * runtime: host memory, memory of another device, and a tensor whose extent
+ * runs past the end of its allocation are refused with PSA_ERR_DEVICE.
+ * Base addresses must be 16-byte aligned.  `stream` is a hipStream_t (NULL =
+ * the null stream).
  *
  * Calls are asynchronous: they validate, enqueue on `stream` and return.
  * Results are valid once the stream has been synchronised.  On any
  * validation failure nothing is enqueued, nothing is written, a status other
  * than PSA_OK is returned and psa_last_error() describes it.  Faults during
  * execution surface at the caller's next synchronisation.  Outputs are fully
- * overwritten (no zero-initialisation is required).  NaN/Inf inputs
- * propagate; they are not trapped.
+ * overwritten (no zero-initialisation is required).
+ *
+ * Non-finite inputs are not trapped.  Device code is built in non-IEEE mode
+ * (max and min need not propagate NaN), so a NaN or Inf in one (batch, head)
+ * slice of the attention inputs leaves that slice's outputs unspecified
+ * (they need not be NaN); every other slice's outputs are exactly those of
+ * a run without it, as no data passes between slices.
  */
 #ifndef PSA_ATTN_H
 #define PSA_ATTN_H
@@ -56,7 +65,10 @@ typedef enum {
   PSA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned       */
   PSA_ERR_ALIAS = 5,       /* an output overlaps an input or other output */
   PSA_ERR_NOMEM = 6,       /* library scratch could not be allocated      */
-  PSA_ERR_HIP = 7          /* a HIP runtime call or launch failed         */
+  PSA_ERR_HIP = 7,         /* a HIP runtime call or launch failed         */
+  PSA_ERR_DEVICE = 8       /* a pointer is not device memory of the
+                              current device, or a tensor's extent runs
+                              past the end of its allocation              */
 } psa_status_t;
 
 /*

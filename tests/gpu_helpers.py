@@ -42,6 +42,19 @@ def round_like(x: np.ndarray, dtype: str) -> np.ndarray:
     return f.astype(np.float64)
 
 
+def stored(x: np.ndarray, dtype: str):
+    """(the float64 values of x once stored in `dtype`, a device tensor
+    holding exactly those values)."""
+    f = np.asarray(x, dtype=np.float32)
+    if dtype == inputs.BF16:
+        bits = inputs.bf16_bits_rne(f)
+        return inputs.bf16_bits_to_f32(bits).astype(np.float64), to_device(None, bits, dtype)
+    if dtype == inputs.F16:
+        bits = inputs.f16_bits_rne(f)
+        return inputs.f16_bits_to_f32(bits).astype(np.float64), to_device(None, bits, dtype)
+    return f.astype(np.float64), to_device(f, None, dtype)
+
+
 def device_inputs(x: inputs.Inputs):
     return to_device(x.qkv, x.qkv_bits, x.wl.dtype), to_device(x.dO, x.dO_bits, x.wl.dtype)
 

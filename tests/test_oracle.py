@@ -235,3 +235,50 @@ def test_max_rel_err_definition():
     got = ref + np.array([[0.0, 0.1], [-0.2, 0.0]])
     assert orc.max_rel_err(got, ref) == pytest.approx(0.2 / 4.0)
     assert orc.max_rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+def test_preprocess_D_by_brute_force(rng):
+    """D_i = rowsum(dO o O) equals sum_j P_ij dP_ij for O = P V, with P and
+    dP = dO V^T formed here element by element by plain loops (the row-sum
+    identity behind dS rows summing to zero), on a tiny batch of slices."""
+    B, H, N, dk, dv, s = 2, 2, 5, 3, 4, 0.8
+    qkv, dO = _rand(rng, B, H, dk, dv, N)
+    o, _ = orc.forward(qkv, dk, dv, s)
+    D = orc.preprocess_D(o, dO)
+    assert D.shape == (B, H, N)
+    for b in range(B):
+        for h in range(H):
+            q, k, v, g = qkv[b, h, :dk], qkv[b, h, dk:2 * dk], qkv[b, h, 2 * dk:], dO[b, h]
+            for i in range(N):
+                sc = [s * sum(q[d, i] * k[d, j] for d in range(dk)) for j in range(N)]
+                z = sum(math.exp(x) for x in sc)
+                want = 0.0
+                for j in range(N):
+                    dp = sum(g[c, i] * v[c, j] for c in range(dv))
+                    want += math.exp(sc[j]) / z * dp
+                assert D[b, h, i] == pytest.approx(want, abs=1e-13)
+
+
+def test_preprocess_D_q_zero_closed_form(rng):
+    """Q = 0: O_i is the key mean of V, so D_i = dO_i . Vbar."""
+    dk, dv, N = 3, 5, 8
+    qkv, dO = _rand(rng, 1, 1, dk, dv, N)
+    qkv[:, :, :dk] = 0.0
+    o, _ = orc.forward(qkv, dk, dv, 0.7)
+    vbar = qkv[0, 0, 2 * dk:].mean(axis=1)
+    np.testing.assert_allclose(orc.preprocess_D(o, dO)[0, 0], vbar @ dO[0, 0], atol=1e-14)
+
+
+def test_preprocess_D_reduces_over_channels_only():
+    """One nonzero channel-token pair in O and dO gives exactly one nonzero D
+    entry, at that token (a sum over tokens or a transposed operand would
+    spread or move it)."""
+    o = np.zeros((1, 2, 3, 4))
+    g = np.zeros((1, 2, 3, 4))
+    o[0, 1, 2, 3] = 1.5
+    g[0, 1, 2, 3] = -2.0
+    g[0, 1, 0, 1] = 7.0  # paired with O = 0: contributes nothing
+    D = orc.preprocess_D(o, g)
+    want = np.zeros((1, 2, 4))
+    want[0, 1, 3] = -3.0
+    np.testing.assert_array_equal(D, want)

@@ -17,7 +17,8 @@ PSA_BF16 = 1
 PSA_F16 = 2
 
 STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPPORTED",
-          4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP"}
+          4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP",
+          8: "PSA_ERR_DEVICE"}
 
 EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_fwd_vslice", "psa_attn_bwd_vslice", "psa_merge_fwd",
            "psa_merge_bwd", "psa_qkv_conv_bwd", "psa_qkv_conv_cat_bwd",
@@ -178,6 +179,21 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _on_gpu(fn: str, *named) -> None:
+    """Every tensor must live on one GPU.  The library receives raw addresses,
+    and a host address handed to a kernel is a GPU memory fault, so this is
+    checked before any library call (and again by the library itself)."""
+    dev = None
+    for name, t in named:
+        if not t.is_cuda:
+            raise ValueError(f"{fn}: {name} is on {t.device}; every tensor must be on a GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{fn}: {name} is on {t.device} but {named[0][0]} is on {dev}; "
+                             "every tensor must be on one GPU")
+
+
 def _check_out(name: str, t, shape, dtype, device) -> None:
     """Caller-provided outputs must be exactly what the library will write."""
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
@@ -220,11 +236,13 @@ def fwd(qkv, dk: int, dv: int, scale: float, out=None):
     """O [B, heads, dv, N] (qkv's dtype) and LSE [B, heads, N] (float32)."""
     import torch
     B, H, N = _shape(qkv, dk, dv)
+    _on_gpu("fwd", ("qkv", qkv))
     if out is None:
         o = torch.empty((B, H, dv, N), dtype=qkv.dtype, device=qkv.device)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
     else:
         o, lse = out
+        _on_gpu("fwd", ("qkv", qkv), ("o", o), ("lse", lse))
         _check_out("o", o, (B, H, dv, N), qkv.dtype, qkv.device)
         _check_out("lse", lse, (B, H, N), torch.float32, qkv.device)
     _check("psa_attn_fwd", psa_attn_fwd(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, dk,
@@ -236,6 +254,7 @@ def bwd(qkv, o, lse, dO, dk: int, dv: int, scale: float, out=None):
     """d_packed [B, heads, 2dk+dv, N]: sections dQ, dK, dV."""
     import torch
     B, H, N = _shape(qkv, dk, dv)
+    _on_gpu("bwd", ("qkv", qkv), ("o", o), ("lse", lse), ("dO", dO), *((("out", out),) if out is not None else ()))
     for name, t in (("o", o), ("lse", lse), ("dO", dO)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -264,6 +283,7 @@ def conv_bwd(x, w, dy, out=None):
     cout = w.shape[0]
     if w.shape[1] != cin or dy.numel() != B * cout * N or dy.shape[0] != B or dy.shape[-1] != N:
         raise ValueError(f"dy must hold [B, cout, N] = [{B}, {cout}, {N}]; got {tuple(dy.shape)}")
+    _on_gpu("conv_bwd", ("x", x), ("w", w), ("dy", dy))
     for name, t in (("x", x), ("w", w), ("dy", dy)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -274,6 +294,7 @@ def conv_bwd(x, w, dy, out=None):
         dw = torch.empty_like(w)
     else:
         dx, dw = out
+        _on_gpu("conv_bwd", ("x", x), ("dx", dx), ("dw", dw))
         _check_out("dx", dx, x.shape, x.dtype, x.device)
         _check_out("dw", dw, w.shape, w.dtype, x.device)
     _check("psa_qkv_conv_bwd", psa_qkv_conv_bwd(x.data_ptr(), w.data_ptr(), dy.data_ptr(), dx.data_ptr(),
@@ -291,6 +312,7 @@ def conv_cat_bwd(x, w, dy, part_channels, out=None):
     cout = w.shape[0]
     if w.shape[1] != cin or dy.numel() != B * cout * N or dy.shape[0] != B or dy.shape[-1] != N:
         raise ValueError(f"dy must hold [B, cout, N] = [{B}, {cout}, {N}]; got {tuple(dy.shape)}")
+    _on_gpu("conv_cat_bwd", ("x", x), ("w", w), ("dy", dy))
     for name, t in (("x", x), ("w", w), ("dy", dy)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -303,6 +325,7 @@ def conv_cat_bwd(x, w, dy, part_channels, out=None):
         dxs, dw = out
         if len(dxs) != len(part_channels):
             raise ValueError("out must hold one dx tensor per part")
+        _on_gpu("conv_cat_bwd", ("x", x), ("dw", dw), *((f"dx[{k}]", d_) for k, d_ in enumerate(dxs)))
         for k, (d_, c) in enumerate(zip(dxs, part_channels)):
             _check_out(f"dx[{k}]", d_, (B, c, N), x.dtype, x.device)
         _check_out("dw", dw, w.shape, w.dtype, x.device)
@@ -319,6 +342,7 @@ def channel_cat_bwd(dy, channels: int, offset: int, out=None):
     import torch
     if dy.dim() < 2 or not dy.is_contiguous():
         raise ValueError("dy must be a contiguous [B, C, ...] tensor")
+    _on_gpu("channel_cat_bwd", ("dy", dy), *((("out", out),) if out is not None else ()))
     B, C = dy.shape[0], dy.shape[1]
     inner = dy[0, 0].numel()
     shape = (B, channels, *dy.shape[2:])
@@ -344,11 +368,13 @@ def fwd_vslice(qkv, dk: int, dv_total: int, v0: int, dv: int, scale: float, out=
     """Attention over V rows [v0, v0+dv): O [B, heads, dv, N] and LSE [B, heads, N]."""
     import torch
     B, H, N = _vslice_shape(qkv, dk, dv_total)
+    _on_gpu("fwd_vslice", ("qkv", qkv))
     if out is None:
         o = torch.empty((B, H, dv, N), dtype=qkv.dtype, device=qkv.device)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
     else:
         o, lse = out
+        _on_gpu("fwd_vslice", ("qkv", qkv), ("o", o), ("lse", lse))
         _check_out("o", o, (B, H, dv, N), qkv.dtype, qkv.device)
         _check_out("lse", lse, (B, H, N), torch.float32, qkv.device)
     _check("psa_attn_fwd_vslice", psa_attn_fwd_vslice(qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, dk,
@@ -363,6 +389,7 @@ def bwd_vslice(qkv, o, lse, dO, d_packed, dk: int, dv_total: int, v0: int, dv: i
     slice overwritten, dQ and dK overwritten or (accumulate) added to."""
     import torch
     B, H, N = _vslice_shape(qkv, dk, dv_total)
+    _on_gpu("bwd_vslice", ("qkv", qkv), ("o", o), ("lse", lse), ("dO", dO), ("d_packed", d_packed))
     for name, t in (("o", o), ("lse", lse), ("dO", dO), ("d_packed", d_packed)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -389,6 +416,7 @@ def merge_fwd(o_lo, o_hi, out=None):
         raise ValueError("o_lo and o_hi must be equal-shaped [B, heads, half, N]")
     if not (o_lo.is_contiguous() and o_hi.is_contiguous()):
         raise ValueError("o_lo and o_hi must be contiguous")
+    _on_gpu("merge_fwd", ("o_lo", o_lo), ("o_hi", o_hi), *((("out", out),) if out is not None else ()))
     B, H, half, N = o_lo.shape
     m = torch.empty((B, H, 2 * half, N), dtype=o_lo.dtype, device=o_lo.device) if out is None else out
     _check_out("merged", m, (B, H, 2 * half, N), o_lo.dtype, o_lo.device)
@@ -402,6 +430,7 @@ def merge_bwd(d_merged, out=None):
     import torch
     if d_merged.dim() != 4 or d_merged.shape[2] % 2 or not d_merged.is_contiguous():
         raise ValueError("d_merged must be a contiguous [B, heads, 2*half, N] tensor")
+    _on_gpu("merge_bwd", ("d_merged", d_merged), *((("d_lo", out[0]), ("d_hi", out[1])) if out is not None else ()))
     B, H, C, N = d_merged.shape
     half = C // 2
     if out is None:

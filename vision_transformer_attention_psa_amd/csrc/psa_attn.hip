@@ -33,66 +33,28 @@ int fail(int code, const std::string& msg) {
 // over more MFMAs; small sequences use 16 per wave so that the grid still
 // fills 256 CUs.  (Measured: 8-wave backward workgroups were slower.)
 // 16-bit fragments (bf16, fp16) take half the registers of fp32 ones and
-// share one set of tiles.  Defaults can be overridden at build time
-// (-DPSA_BF16_FWD_QB=...) for tuning.
-#ifndef PSA_BF16_FWD_QB
-#define PSA_BF16_FWD_QB 2
-#endif
-#ifndef PSA_BF16_FWD_NW
-#define PSA_BF16_FWD_NW 8
-#endif
-#ifndef PSA_BF16_FWD_BN
-#define PSA_BF16_FWD_BN 64  // 128-key tiles measured 16% slower at N = 6400
-#endif
-#ifndef PSA_FWD_DK64_48
-#define PSA_FWD_DK64_48 1
-#endif
-#ifndef PSA_BF16_BWD_NW
-#define PSA_BF16_BWD_NW 4
-#endif
-#ifndef PSA_BF16_DKDV_KB
-#define PSA_BF16_DKDV_KB 2
-#endif
-#ifndef PSA_BF16_DKDV_KB_DK64
-#define PSA_BF16_DKDV_KB_DK64 3
-#endif
-#ifndef PSA_BF16_DKDV_BMQ
-#define PSA_BF16_DKDV_BMQ 64
-#endif
-#ifndef PSA_BF16_DQ_QB
-#define PSA_BF16_DQ_QB 2
-#endif
-#ifndef PSA_BF16_DQ_BN
-#define PSA_BF16_DQ_BN 64
-#endif
-#ifndef PSA_BF16_DQ_BN_DK64
-#define PSA_BF16_DQ_BN_DK64 128
-#endif
-// dK/dV body: query tiles prefetched two iterations ahead (the thread halves
-// take turns).  Measured -4% at N = 400, -3% at N = 1600, -0.7% at N = 6400;
-// the same for the dQ body's and the forward's key tiles measured no gain.
-#ifndef PSA_DKDV_DEEP
-#define PSA_DKDV_DEEP 1
-#endif
-#ifndef PSA_BWD_SPLIT
-#define PSA_BWD_SPLIT 0  // 1: separate dK/dV and dQ launches (per-pass timing)
-#endif
-#ifndef PSA_SMALL_N_MAX
-#define PSA_SMALL_N_MAX 512  // forward: sequences up to this length use the narrow tiles
-#endif
+// share one set of tiles.
+constexpr int kFwdQB = 2, kFwdNW = 8;
+constexpr int kFwdBN = 64;  // 128-key tiles measured 16% slower at N = 6400
+constexpr int kBwdNW = 4;
+constexpr int kDkdvKB = 2, kDkdvKBDk64 = 3, kDkdvBMQ = 64;
+constexpr int kDqQB = 2, kDqBN = 64, kDqBNDk64 = 128;
+// Forward: sequences up to this length use the narrow tiles.
+constexpr int kSmallNMax = 512;
 // Backward: measured at B*heads = 64 (dk 32, dv 64), the narrow tiles win up
 // to N = 256 (13.3 vs 13.9 us) and the wide ones from N = 320 (16.8 vs 17.8 us;
 // N = 400: 22.3 vs 24.2 us, N = 512: 24.2 vs 27.6 us).
-#ifndef PSA_SMALL_N_MAX_BWD
-#define PSA_SMALL_N_MAX_BWD 256
-#endif
+constexpr int kSmallNMaxBwd = 256;
 // Head dims with dk + dv > 128 ("wide heads") halve the per-wave register
 // tiles (their accumulators and stationary fragments are twice as large)
 // and the streamed LDS tiles (their rows are twice as long), so that two
 // workgroups still fit one CU.
 template <int DK, int DV> constexpr bool wide_heads() { return DK + DV > 128; }
-// The dK/dV two-deep prefetch costs no registers only while one streamed
-// Q|dO tile (4-channel x 8-token blocks) needs at most half of the threads.
+// dK/dV body: query tiles prefetched two iterations ahead (the thread halves
+// take turns; measured -4% at N = 400, -3% at N = 1600, -0.7% at N = 6400;
+// the same for the dQ body's and the forward's key tiles measured no gain).
+// It costs no registers only while one streamed Q|dO tile (4-channel x
+// 8-token blocks) needs at most half of the threads.
 template <int DK, int DV, int BMQ, int NW> constexpr bool deep_fits() {
   return (DK + DV) / 4 * (BMQ / 8) <= NW * 32;
 }
@@ -103,10 +65,10 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   // (172 registers otherwise) reuse each K/V fragment 1.5x as often as 8
   // waves of 32 (427-429 vs 440-441 us at N = 6400); at dk = 32 the 8-wave
   // tiles stay (67-69 vs 59 us at N = 1600).
-  static constexpr bool F48 = !W && DK > 32 && PSA_FWD_DK64_48;
-  static constexpr int FWD_NW = F48 ? 4 : PSA_BF16_FWD_NW, FWD_QB = W ? 2 : (F48 ? 3 : PSA_BF16_FWD_QB),
-                       FWD_BN = W ? 64 : PSA_BF16_FWD_BN, FWD_OCC = F48 ? 3 : 0;
-  static constexpr int BWD_NW = PSA_BF16_BWD_NW;
+  static constexpr bool F48 = !W && DK > 32;
+  static constexpr int FWD_NW = F48 ? 4 : kFwdNW, FWD_QB = W ? 2 : (F48 ? 3 : kFwdQB),
+                       FWD_BN = W ? 64 : kFwdBN, FWD_OCC = F48 ? 3 : 0;
+  static constexpr int BWD_NW = kBwdNW;
   // dk = 32: 32-query dK/dV tiles bring the kernel to about 162 registers,
   // three waves per SIMD (measured 5% faster at N = 1600); dk = 64 stays at
   // two waves per SIMD either way and runs faster with 64-query tiles.
@@ -114,17 +76,16 @@ template <typename T, int DK, int DV> struct TilesWide {  // bf16 and fp16
   // MFMAs instead of two) at 246 registers, with the one-tile prefetch (the
   // two-deep one would need 270): 1126 vs 1168 us at N = 6400.  At dk = 32
   // the 32-key waves with the two-deep prefetch stay faster.
-  static constexpr int DKDV_KB = W ? 1 : (DK <= 32 ? PSA_BF16_DKDV_KB : PSA_BF16_DKDV_KB_DK64);
-  static constexpr int DKDV_BMQ = W ? 32 : (DK <= 32 ? 32 : PSA_BF16_DKDV_BMQ);
+  static constexpr int DKDV_KB = W ? 1 : (DK <= 32 ? kDkdvKB : kDkdvKBDk64);
+  static constexpr int DKDV_BMQ = W ? 32 : (DK <= 32 ? 32 : kDkdvBMQ);
   // dk = 64: 48 queries per dQ wave fit within the registers the dK/dV body
   // already needs, so the launch keeps two waves per SIMD with 1.5x the reuse
   // of each K/V fragment (measured 3% faster at N = 6400); at dk = 32 the
   // extra registers would cost a wave per SIMD.  dk = 64: 128-key dQ tiles
   // (half the barriers per key; same registers, 70 KB of LDS) measured
   // 1044 vs 1059 us at N = 6400; at dk = 32 they cost 2-6%.
-  static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? PSA_BF16_DQ_QB : 3),
-                       DQ_BN = W ? 32 : (DK <= 32 ? PSA_BF16_DQ_BN : PSA_BF16_DQ_BN_DK64);
-  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && DKDV_KB <= 2 && deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
+  static constexpr int DQ_QB = W ? 1 : (DK <= 32 ? kDqQB : 3), DQ_BN = W ? 32 : (DK <= 32 ? kDqBN : kDqBNDk64);
+  static constexpr bool DKDV_DEEP = DKDV_KB <= 2 && deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
 };
 template <int DK, int DV> struct TilesWide<float, DK, DV> {
   static constexpr int FWD_NW = 4, FWD_QB = 1, FWD_BN = 32, FWD_OCC = 0;
@@ -142,13 +103,13 @@ template <typename T, int DK, int DV> struct TilesNarrow {  // bf16 and fp16
   static constexpr int BWD_NW = 4;
   static constexpr int DKDV_KB = 1, DKDV_BMQ = 32;
   static constexpr int DQ_QB = 1, DQ_BN = W ? 32 : 64;
-  static constexpr bool DKDV_DEEP = PSA_DKDV_DEEP && deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
+  static constexpr bool DKDV_DEEP = deep_fits<DK, DV, DKDV_BMQ, BWD_NW>();
 };
 template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, DK, DV> {};
 
 // ------------------------------------------------------- per-kernel timing
-// Slots: forward; D/LSE preprocessing; the backward GEMM launch (fused dK/dV
-// + dQ, or dK/dV alone when split); dQ when split; the 1x1-conv backward's
+// Slots: forward; D/LSE preprocessing; the backward GEMM launch (dK/dV and
+// dQ in one grid); the dQ reduction; the 1x1-conv backward's
 // dx GEMM; its dw GEMM (with the split reduction); the channel-cat slice copy;
 // the PSA merge forward and backward copies.
 enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5, K_CAT = 6, K_MERGE_FWD = 7,
@@ -298,28 +259,6 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
     rc = check_launch("psa_attn_bwd preprocess launch");
   }
   if (rc != PSA_OK) return rc;
-#if PSA_BWD_SPLIT
-  {
-    TimedLaunch tl(K_MAIN, st);
-    if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, true, C::DKDV_DEEP>), dim3(nkb), dim3(NW * 64),
-                         0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
-    else
-      hipLaunchKernelGGL((psa::psa_bwd_dkdv_kernel<T, DK, DV, C::DKDV_KB, NW, C::DKDV_BMQ, false, C::DKDV_DEEP>), dim3(nkb),
-                         dim3(NW * 64), 0, st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nkb, c, scale, pv);
-    rc = check_launch("psa_attn_bwd dK/dV launch");
-  }
-  if (rc == PSA_OK) {
-    TimedLaunch tl(K_DQ, st);
-    if (vec_ok<T>(N))
-      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, NW, C::DQ_BN, true>), dim3(nqb), dim3(NW * 64), 0, st,
-                         (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale, pv);
-    else
-      hipLaunchKernelGGL((psa::psa_bwd_dq_kernel<T, DK, DV, C::DQ_QB, NW, C::DQ_BN, false>), dim3(nqb), dim3(NW * 64), 0,
-                         st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nqt, nqb, c, scale, pv);
-    rc = check_launch("psa_attn_bwd dQ launch");
-  }
-#else
   {
     TimedLaunch tl(K_MAIN, st);
     const dim3 grid((unsigned)(nkb + nqb)), block(NW * 64);
@@ -333,7 +272,6 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
     rc = check_launch("psa_attn_bwd launch");
   }
-#endif
   return rc;
 }
 
@@ -508,7 +446,8 @@ int validate_common(const char* fn, int B, int heads, int N, int dk, int dv, flo
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
 // gfx950 is the only compiled target; refuse other devices before any launch.
-int check_device(const char* fn) {
+// On success *dev_out is the current device.
+int check_device(const char* fn, int* dev_out) {
   static std::mutex mu;
   static int known[64] = {0};  // 0 unknown, 1 ok, 2 wrong arch
   int dev = 0;
@@ -522,6 +461,46 @@ int check_device(const char* fn) {
     known[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : 2;
   }
   if (known[dev] != 1) return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": device is not gfx950");
+  *dev_out = dev;
+  return PSA_OK;
+}
+
+// One caller buffer: its name for messages, base address and extent.
+struct Buf {
+  const char* name;
+  Range r;
+};
+
+// Every buffer must be memory the GPU can address as device memory of the
+// current device (a host address handed to a kernel faults the GPU), and its
+// whole extent must lie inside one allocation (an undersized buffer would be
+// written past its end).  A failed query leaves HIP's last-error state
+// cleared, so that the launch checks that follow see only their own errors.
+int check_buffers(const char* fn, int dev, const Buf* bufs, int n) {
+  for (int k = 0; k < n; ++k) {
+    const Buf& b = bufs[k];
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, (const void*)b.r.lo) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PSA_ERR_DEVICE, std::string(fn) + ": " + b.name + " is not device memory");
+    }
+    const bool managed = a.type == hipMemoryTypeManaged || a.type == hipMemoryTypeUnified || a.isManaged;
+    if (!managed && a.type != hipMemoryTypeDevice)
+      return fail(PSA_ERR_DEVICE, std::string(fn) + ": " + b.name + " is not device memory");
+    if (!managed && a.device != dev)
+      return fail(PSA_ERR_DEVICE, std::string(fn) + ": " + b.name + " is on device " + std::to_string(a.device) +
+                                      ", not the current device " + std::to_string(dev));
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)b.r.lo) == hipSuccess) {
+      if (b.r.hi > (uintptr_t)base + size)
+        return fail(PSA_ERR_DEVICE, std::string(fn) + ": " + b.name + " extends past the end of its allocation (" +
+                                        std::to_string(b.r.hi - b.r.lo) + " bytes needed, " +
+                                        std::to_string((uintptr_t)base + size - b.r.lo) + " available)");
+    } else {
+      (void)hipGetLastError();
+    }
+  }
   return PSA_OK;
 }
 
@@ -550,12 +529,15 @@ int attn_fwd_impl(const char* fn, const void* qkv, void* o, float* lse, int B, i
   const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
   if (overlap(ro, rq) || overlap(rl, rq) || overlap(ro, rl))
     return fail(PSA_ERR_ALIAS, std::string(fn) + ": o, lse and qkv must not overlap");
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  int dev = 0;
+  if ((rc = check_device(fn, &dev)) != PSA_OK) return rc;
+  const Buf bufs[] = {{"qkv", rq}, {"o", ro}, {"lse", rl}};
+  if ((rc = check_buffers(fn, dev, bufs, 3)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, 0};
 #define X(DT, T, K, V)                                                                                   \
   if (dtype == DT && dk == K && dv == V)                                                                 \
-    return N <= PSA_SMALL_N_MAX ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st) \
+    return N <= kSmallNMax ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st) \
                                 : run_fwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st);
   PSA_INSTANCES(X)
 #undef X
@@ -583,12 +565,15 @@ int attn_bwd_impl(const char* fn, const void* qkv, const void* o, const float* l
   const Range rl{(uintptr_t)lse, (uintptr_t)lse + BH * N * 4};
   if (overlap(rd, rq) || overlap(rd, ro) || overlap(rd, rg) || overlap(rd, rl))
     return fail(PSA_ERR_ALIAS, std::string(fn) + ": d_packed must not overlap any input");
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  int dev = 0;
+  if ((rc = check_device(fn, &dev)) != PSA_OK) return rc;
+  const Buf bufs[] = {{"qkv", rq}, {"o", ro}, {"lse", rl}, {"dO", rg}, {"d_packed", rd}};
+  if ((rc = check_buffers(fn, dev, bufs, 5)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, accum ? 1 : 0};
 #define X(DT, T, K, V)                                                                                        \
   if (dtype == DT && dk == K && dv == V)                                                                      \
-    return N <= PSA_SMALL_N_MAX_BWD                                                                           \
+    return N <= kSmallNMaxBwd                                                                           \
                ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st) \
                : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st);
   PSA_INSTANCES(X)
@@ -637,8 +622,13 @@ int conv_bwd_impl(const char* fn, const void* x, const void* w, const void* dy, 
     for (int q = 0; q < k; ++q)
       if (overlap(outs[k], outs[q])) return fail(PSA_ERR_ALIAS, std::string(fn) + ": outputs must not overlap");
   }
-  int rc;
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  int rc, dev = 0;
+  if ((rc = check_device(fn, &dev)) != PSA_OK) return rc;
+  {
+    Buf bufs[3 + 1 + psa::kCatMaxParts] = {{"x", rx}, {"w", rw}, {"dy", ry}, {"dw", rdw}};
+    for (int k = 0; k < n_parts; ++k) bufs[4 + k] = Buf{"dx", outs[k + 1]};
+    if ((rc = check_buffers(fn, dev, bufs, 4 + n_parts)) != PSA_OK) return rc;
+  }
   hipStream_t st = (hipStream_t)stream;
   auto go = [&](auto tag) {
     using T = decltype(tag);
@@ -764,8 +754,10 @@ int psa_channel_cat_bwd(const void* dy, void* dx, int n_outer, int chunk, int to
   const Range ry{(uintptr_t)dy, (uintptr_t)dy + (size_t)n_outer * total * e};
   const Range rx{(uintptr_t)dx, (uintptr_t)dx + (size_t)n_outer * chunk * e};
   if (overlap(rx, ry)) return fail(PSA_ERR_ALIAS, "psa_channel_cat_bwd: dx must not overlap dy");
-  int rc;
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  int rc, dev = 0;
+  if ((rc = check_device(fn, &dev)) != PSA_OK) return rc;
+  const Buf bufs[] = {{"dy", ry}, {"dx", rx}};
+  if ((rc = check_buffers(fn, dev, bufs, 2)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == PSA_F32) return run_channel_cat_bwd<float>(dy, dx, n_outer, chunk, total, offset, st);
   if (dtype == PSA_BF16) return run_channel_cat_bwd<psa::bf16>(dy, dx, n_outer, chunk, total, offset, st);
@@ -789,8 +781,10 @@ static int merge_impl(bool forward, const char* fn, const void* lo, const void* 
   const Range rm{(uintptr_t)merged, (uintptr_t)merged + 2 * part};
   if (overlap(rlo, rhi) || overlap(rlo, rm) || overlap(rhi, rm))
     return fail(PSA_ERR_ALIAS, std::string(fn) + ": lo, hi and merged must not overlap");
-  int rc;
-  if ((rc = check_device(fn)) != PSA_OK) return rc;
+  int rc, dev = 0;
+  if ((rc = check_device(fn, &dev)) != PSA_OK) return rc;
+  const Buf bufs[] = {{"lo", rlo}, {"hi", rhi}, {"merged", rm}};
+  if ((rc = check_buffers(fn, dev, bufs, 3)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == PSA_F32) return run_merge<float>(forward, lo, hi, merged, (int)BH, half, N, st);
   if (dtype == PSA_BF16) return run_merge<psa::bf16>(forward, lo, hi, merged, (int)BH, half, N, st);

@@ -7,11 +7,11 @@
 // need are
 //   frag_ch  : rows = channels, contraction over 32 tokens.  Read straight
 //              from a channel-major LDS tile ([channel][token]).
-//   frag_tok : rows = tokens, contraction over 32 channels.  16-bit types read it
-//              from a token-major LDS copy ([token][channel]) that the
-//              staging code writes once per tile (in-register 4x8 block
-//              transpose); fp32 gathers it from the channel-major tile.
-// Both are one 16-byte LDS read per lane for 16-bit types (bf16, fp16).
+//   frag_tr  : rows = tokens, contraction over 32 channels, read from the
+//              same channel-major tile with the gfx950 transpose read (16-bit
+//              types, two 8-byte reads per lane); fp32 gathers it element by
+//              element (frag_tok).
+// frag_ch is one 16-byte LDS read per lane for 16-bit types (bf16, fp16).
 //
 // Chaining: a 16x16 fp32 accumulator block holds row 4*g + r of column
 // (lane & 15) in register r.  Score tiles are computed over 32-token chunks
@@ -101,68 +101,19 @@ __device__ __forceinline__ int lane_id() { return thread_id() & 63; }
 // Token of row m (0..15) of score block h within a 32-token chunk.
 __device__ __forceinline__ int perm_row(int m, int h) { return 8 * (m >> 2) + 4 * h + (m & 3); }
 
-// Token-major tiles: element (token r, channel ch) lives at
-//   r * ldt + 32 * (r / 16) + ch,   ldt = channels + 8.
-// The odd pitch (in 16-byte units) separates 16 consecutive rows; the extra
-// 64-byte skew every 16 rows separates rows r and r + 16, which one permuted
-// fragment read (rows 8a + b + 4h) touches together.  With it, fragment reads
-// and the staging writes are free of LDS bank conflicts for every tile width.
-__device__ __forceinline__ int tm_off(int r, int ch, int ldt) { return r * ldt + 32 * (r >> 4) + ch; }
-constexpr int tm_elems(int rows, int ldt) { return rows * ldt + 32 * ((rows + 15) / 16); }
-
-// Rows = tokens row0 + (PERM ? perm_row(lane&15, h) : lane&15); contraction
-// over channels k0 .. k0+31 of a tensor with CV channels (CV % 16 == 0; the
-// upper half of a chunk past CV reads as zero).
-// 16-bit types: token-major tile (see tm_off).  fp32: channel-major tile
-// nat[ch][token], pitch ldn.
-template <int CV, bool PERM, typename T>
-__device__ __forceinline__ void frag_tok(Frag<T>& f, const T* tm, int ldt, const T*, int, int row0, int h,
-                                         int k0) {
-  static_assert(is_16bit<T>(), "16-bit element type");
-  typedef typename Vec8<T>::type V8;
-  const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  const int row = row0 + (PERM ? perm_row(t, h) : t);
-  if (CV % 32 == 0 || k0 + 8 * g < CV) {
-    f.v = *(const V8*)(tm + tm_off(row, k0 + 8 * g, ldt));
-  } else {
-    f.v = V8{(T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f, (T)0.f};
-  }
-}
-template <int CV, bool PERM>
-__device__ __forceinline__ void frag_tok(Frag<float>& f, const float*, int, const float* nat, int ldn, int row0,
-                                         int h, int k0) {
-  const int lane = lane_id(), t = lane & 15, g = lane >> 4;
-  const int tok = row0 + (PERM ? perm_row(t, h) : t);
-  const bool live = CV % 32 == 0 || k0 + 8 * g < CV;
-  const float* p = nat + (k0 + 8 * g) * ldn + tok;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f.v[s] = live ? p[s * ldn] : 0.f;
-}
-
-// The fragment frag_tok reads, taken from the channel-major tile nat[ch][token]
-// (pitch ldn) with the gfx950 transpose read ds_read_b64_tr_b16: within each
-// group of 16 lanes, lane i receives as its element e (of 4) the 16-bit value
-// at position i % 4 of the 8 bytes that lane 4e + i/4 addressed.  So lane
-// (t, g) addresses one channel row at the 4 consecutive tokens that result
-// lanes 4(t%4) .. 4(t%4)+3 hold, and two reads give lane (t, g) eight channels
-// of its token.
-// PSA_TR_ILV (default): the first read takes channels k0 + 8g + {0, 1, 4, 5},
-// the second {2, 3, 6, 7}, so that the four rows one read touches are spread
-// over the banks (consecutive rows, 16 bytes apart within each row, meet at
-// the same banks); the fragment then holds its channels in the order
-// 0 1 4 5 2 3 6 7, which is harmless as long as the other MFMA operand is
-// read with frag_tr as well.  Otherwise the reads take {0..3} and {4..7}.
-#ifndef PSA_TR_ILV
-#define PSA_TR_ILV 1
-#endif
-// 16-bit tiles are staged channel-major only, and the contractions over
-// channels read them with frag_tr.  Bit mask of the kernels that do so:
-// 1 dK/dV body, 2 dQ body, 4 forward, 8 convolution dx.
-#ifndef PSA_TR_READS
-#define PSA_TR_READS 15
-#endif
-constexpr int kTrDkdv = 1, kTrDq = 2, kTrFwd = 4, kTrConvDx = 8;
-template <typename T, int BODY> constexpr bool tr_reads() { return (PSA_TR_READS & BODY) && is_16bit<T>(); }
+// Token rows, channel contraction (see frag_tok), read from a 16-bit channel-major tile
+// nat[ch][token] (pitch ldn) with the gfx950 transpose read
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives as its
+// element e (of 4) the 16-bit value at position i % 4 of the 8 bytes that
+// lane 4e + i/4 addressed.  So lane (t, g) addresses one channel row at the
+// 4 consecutive tokens that result lanes 4(t%4) .. 4(t%4)+3 hold, and two
+// reads give lane (t, g) eight channels of its token.
+// The first read takes channels k0 + 8g + {0, 1, 4, 5}, the second
+// {2, 3, 6, 7}, so that the four rows one read touches are spread over the
+// banks (consecutive rows, 16 bytes apart within each row, meet at the same
+// banks); the fragment then holds its channels in the order 0 1 4 5 2 3 6 7,
+// which is harmless because both operands of every channel contraction are
+// read this way.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 template <int CV, bool PERM, typename T>
@@ -171,12 +122,31 @@ __device__ __forceinline__ void frag_tr(Frag<T>& f, const T* nat, int ldn, int r
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const int lane = lane_id(), t = lane & 15, g = lane >> 4, e = t >> 2;
   const int tok = row0 + (PERM ? 8 * (t & 3) + 4 * h : 4 * (t & 3));
-  const int ch = k0 + 8 * g + (PSA_TR_ILV ? (e & 1) + 4 * (e >> 1) : e);
+  const int ch = k0 + 8 * g + (e & 1) + 4 * (e >> 1);
   const T* p = nat + ch * ldn + tok;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (PSA_TR_ILV ? 2 : 4) * ldn));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2 * ldn));
   const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   f.v = __builtin_bit_cast(typename Vec8<T>::type, v);
+}
+
+// Rows = tokens row0 + (PERM ? perm_row(lane&15, h) : lane&15); contraction
+// over channels k0 .. k0+31 of a tensor with CV channels, from the
+// channel-major tile nat[ch][token] (pitch ldn): transpose reads for 16-bit
+// types; fp32 gathers element by element (CV % 16 == 0; the upper half of a
+// chunk past CV reads as zero).
+template <int CV, bool PERM, typename T>
+__device__ __forceinline__ void frag_tok(Frag<T>& f, const T* nat, int ldn, int row0, int h, int k0) {
+  if constexpr (is_16bit<T>()) {
+    frag_tr<CV, PERM>(f, nat, ldn, row0, h, k0);
+  } else {
+    const int lane = lane_id(), t = lane & 15, g = lane >> 4;
+    const int tok = row0 + (PERM ? perm_row(t, h) : t);
+    const bool live = CV % 32 == 0 || k0 + 8 * g < CV;
+    const float* p = nat + (k0 + 8 * g) * ldn + tok;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f.v[s] = live ? p[s * ldn] : 0.f;
+  }
 }
 
 // Rows = channels ch0 .. ch0+15, contraction over tokens tok0 + 8g .. +7.
@@ -195,14 +165,6 @@ __device__ __forceinline__ void frag_ch(Frag<float>& f, const float* nat, int ld
     f.v[s] = lo[s];
     f.v[4 + s] = hi[s];
   }
-}
-
-// Empty asm that consumes a fragment: marks it live at this point so that the
-// code computing it is not moved below later control flow.
-template <typename T> __device__ __forceinline__ void pin(const Frag<T>& f) { asm volatile("" ::"v"(f.v)); }
-__device__ __forceinline__ void pin(const Frag<float>& f) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(f.v[s]));
 }
 
 // Max over the four lanes l, l^16, l^32, l^48 (the four row groups holding
@@ -231,41 +193,29 @@ __device__ __forceinline__ void acc_to_frag(Frag<float>& f, const f32x4& a0, con
 // ------------------------------------------------------------------ staging
 // Pitches (elements): 16 bytes of padding per row keeps every row 16-byte
 // aligned and spreads the 16 rows one fragment read touches over all banks.
-#ifndef PSA_NAT_PAD16
-#define PSA_NAT_PAD16 8
-#endif
-template <typename T> constexpr int nat_pitch(int tokens) {
-  return tokens + (sizeof(T) == 2 ? PSA_NAT_PAD16 : 16 / (int)sizeof(T));
-}
-constexpr int tm_pitch(int channels) { return channels + 8; }
+template <typename T> constexpr int nat_pitch(int tokens) { return tokens + 16 / (int)sizeof(T); }
 
 // Global -> registers -> LDS for a tile of C channel rows x BT tokens from
 // token j0 (tokens >= N read as zero).  Rows [0, SPLIT) come from src_lo and
 // rows [SPLIT, C) from src_hi, both channel-major with row stride N.
+// All C rows go to the channel-major tile nat[row][nat_pitch(BT)].
 //   bf16, fp16: each thread owns 4-channel x 8-token blocks (four 16-byte loads).
-//         Rows in [NAT_LO, NAT_HI) go to a channel-major tile
-//         nat[row - NAT_LO][nat_pitch(BT)]; rows in [0, TM_HI) are also
-//         transposed in registers into a token-major tile tm[token][row]
-//         (pitch tm_pitch(TM_HI)).
-//   fp32: 16-byte chunks (4 tokens of one row); all C rows go to the
-//         channel-major tile (token-major reads gather from it instead).
+//   fp32: 16-byte chunks (4 tokens of one row).
 // VECOK: N is a multiple of the 16-byte vector, so every chunk is aligned and
 // wholly inside or wholly past the row end.
-template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
+template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT>
 struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   static_assert(is_16bit<T>(), "16-bit element type");
   static constexpr int CG = C / 4, TC = BT / 8, NB = CG * TC, PER = (NB + NT - 1) / NT;
-  static constexpr int LDN = nat_pitch<T>(BT), LDT = tm_pitch(TM_HI);
-  static constexpr int NAT_ELEMS = (NAT_HI - NAT_LO) * LDN, TM_ELEMS = TM_HI > 0 ? tm_elems(BT, LDT) : 0;
+  static constexpr int LDN = nat_pitch<T>(BT);
+  static constexpr int NAT_ELEMS = C * LDN;
   // Block q: 4 consecutive blocks run along the tokens of one 4-row group
   // (64 contiguous bytes per row in HBM), then the next row group.
   static constexpr int TCL = TC < 4 ? TC : 4;
   static_assert(TC % TCL == 0, "token chunks");
   __device__ static __forceinline__ int blk_tc(int q) { return q % TCL + TCL * (q / (TCL * CG)); }
   __device__ static __forceinline__ int blk_cg(int q) { return (q / TCL) % CG; }
-  static constexpr int NAT_BASE = NAT_LO;  // channel of the first natural row
-  static_assert(C % 4 == 0 && BT % 8 == 0 && SPLIT % 4 == 0 && TM_HI % 4 == 0 && NAT_LO % 4 == 0 &&
-                    NAT_HI % 4 == 0, "tile shape");
+  static_assert(C % 4 == 0 && BT % 8 == 0 && SPLIT % 4 == 0, "tile shape");
   u32x4 r[PER][4];
 
   // One 16-byte chunk (8 tokens of one row) per (u, i); W bytes per load:
@@ -320,39 +270,23 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
       load_w<2>(lo, hi, N, j0, tid);
     }
   }
-  __device__ __forceinline__ void store(T* nat, T* tm, int tid) const {
+  __device__ __forceinline__ void store(T* nat, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
       if (NB % NT != 0 && q >= NB) continue;
-      const int tc = blk_tc(q), cg = blk_cg(q), row = 4 * cg;
-      if (NAT_HI > NAT_LO && row >= NAT_LO && row < NAT_HI) {
+      const int tc = blk_tc(q), row = 4 * blk_cg(q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(nat + (row - NAT_LO + i) * LDN + 8 * tc) = r[u][i];
-      }
-      if (row < TM_HI) {
-        // token 8*tc + e receives rows row..row+3: halves e%2 of dword e/2.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = e >> 1;
-          // v_perm_b32 picks bytes of {hi, lo}: 0-3 from lo, 4-7 from hi.
-          // Even e: low halves of the two rows, odd e: high halves.
-          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const unsigned w0 = __builtin_amdgcn_perm(r[u][1][d], r[u][0][d], sel);
-          const unsigned w1 = __builtin_amdgcn_perm(r[u][3][d], r[u][2][d], sel);
-          *(u32x2*)(tm + tm_off(8 * tc + e, row, LDT)) = u32x2{w0, w1};
-        }
-      }
+      for (int i = 0; i < 4; ++i) *(u32x4*)(nat + (row + i) * LDN + 8 * tc) = r[u][i];
     }
   }
 };
 
-template <int C, int BT, int NT, bool VECOK, int SPLIT, int TM_HI, int NAT_LO, int NAT_HI>
-struct Stager<float, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
+template <int C, int BT, int NT, bool VECOK, int SPLIT>
+struct Stager<float, C, BT, NT, VECOK, SPLIT> {
   static constexpr int CPR = BT / 4, CHUNKS = C * CPR, PER = (CHUNKS + NT - 1) / NT;
-  static constexpr int LDN = nat_pitch<float>(BT), LDT = 0;
-  static constexpr int NAT_ELEMS = C * LDN, TM_ELEMS = 0;
-  static constexpr int NAT_BASE = 0;
+  static constexpr int LDN = nat_pitch<float>(BT);
+  static constexpr int NAT_ELEMS = C * LDN;
   static_assert(BT % 4 == 0, "tile shape");
   f32x4 r[PER];
 
@@ -373,7 +307,7 @@ struct Stager<float, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
       }
     }
   }
-  __device__ __forceinline__ void store(float* nat, float*, int tid) const {
+  __device__ __forceinline__ void store(float* nat, int tid) const {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
@@ -383,15 +317,6 @@ struct Stager<float, C, BT, NT, VECOK, SPLIT, TM_HI, NAT_LO, NAT_HI> {
     }
   }
 };
-
-// Workgroup barrier that orders LDS accesses only: global loads still in
-// flight (prefetches into registers) are not waited for, unlike
-// __syncthreads(), whose fence also covers global memory.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Remap so
 // that consecutive logical ids (tiles of one (batch, head) slice, which share

@@ -13,8 +13,8 @@
 // Both GEMMs run on MFMA with 4 waves per workgroup, each owning a 64 x 64
 // output tile (2 x 2 waves: 128 x 128 per workgroup).
 //   dx: contraction over co, which is the slow index of both w and dy: both
-//       tiles are staged channel-major (rows co) and read with the transpose
-//       read (frag_tr), or staged token-major and read with frag_tok.
+//       tiles are staged channel-major (rows co) and read as token rows
+//       (frag_tok: the transpose read for 16-bit types).
 //   dw: contraction over n, the fast index of both dy and x: both tiles are
 //       channel-major and read with frag_ch, as the attention's dV/dK GEMMs.
 #pragma once
@@ -29,8 +29,7 @@ constexpr int kConvTile = 128;  // output rows and columns per workgroup
 // ------------------------------------------------------------------- dx
 // Workgroup: batch b, ci tile [ci0, ci0 + 128), token tile [n0, n0 + 128).
 // co is consumed in chunks of KCH (64, fp32: 32) through a double-buffered
-// pair of tiles holding w^T [128 ci][KCH co] and dy^T [128 n][KCH co]
-// (token-major for 16-bit types; fp32 keeps them channel-major and gathers).
+// pair of channel-major tiles holding w [KCH co][128 ci] and dy [KCH co][128 n].
 //
 // Channel-cat fold (ChannelCatBackward page, struct description): when x is
 // the channel concatenation of up to kCatMaxParts inputs, x = cat(x_0, ...),
@@ -53,13 +52,10 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
                                                           int n_ntiles, int n_citiles, int n_blocks) {
   constexpr int KCH = is_16bit<T>() ? 64 : 32, BT = kConvTile, NT = 256;  // fp32 tiles are twice as wide
   constexpr int KC = KCH / 32;
-  // rows = co (channels of the chunk), tokens = ci (w) or n (dy); with
-  // transpose reads both tiles stay channel-major and frag_tr reads them.
-  constexpr bool TR = tr_reads<T, kTrConvDx>();
-  constexpr int TMR = is_16bit<T>() && !TR ? KCH : 0, NATR = KCH - TMR;
-  using SW = Stager<T, KCH, BT, NT, true, KCH, TMR, 0, NATR>;
-  using SY = Stager<T, KCH, BT, NT, VECOK, KCH, TMR, 0, NATR>;
-  constexpr int BUF = SW::NAT_ELEMS + SW::TM_ELEMS;  // one operand tile
+  // rows = co (channels of the chunk), tokens = ci (w) or n (dy)
+  using SW = Stager<T, KCH, BT, NT, true, KCH>;
+  using SY = Stager<T, KCH, BT, NT, VECOK, KCH>;
+  constexpr int BUF = SW::NAT_ELEMS;  // one operand tile
   __shared__ __attribute__((aligned(16))) T smem[4 * BUF];
 
   const int tid = thread_id(), wv = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -84,8 +80,8 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
   auto stage = [&](int slot) {
     T* a = smem + slot * 2 * BUF;
     T* y = a + BUF;
-    sw.store(a, a + SW::NAT_ELEMS, tid);
-    sy.store(y, y + SY::NAT_ELEMS, tid);
+    sw.store(a, tid);
+    sy.store(y, tid);
   };
   sw.load(w, w, cin, ci0, tid);
   sy.load(dyb, dyb, N, n0, tid);
@@ -104,19 +100,9 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
     for (int kc = 0; kc < KC; ++kc) {
       Frag<T> fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (TR)
-          frag_tr<KCH, false>(fa[i], a, SW::LDN, wr + 16 * i, 0, 32 * kc);
-        else
-          frag_tok<KCH, false>(fa[i], a + SW::NAT_ELEMS, SW::LDT, a, SW::LDN, wr + 16 * i, 0, 32 * kc);
-      }
+      for (int i = 0; i < 4; ++i) frag_tok<KCH, false>(fa[i], a, SW::LDN, wr + 16 * i, 0, 32 * kc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (TR)
-          frag_tr<KCH, false>(fb[j], y, SY::LDN, wc + 16 * j, 0, 32 * kc);
-        else
-          frag_tok<KCH, false>(fb[j], y + SY::NAT_ELEMS, SY::LDT, y, SY::LDN, wc + 16 * j, 0, 32 * kc);
-      }
+      for (int j = 0; j < 4; ++j) frag_tok<KCH, false>(fb[j], y, SY::LDN, wc + 16 * j, 0, 32 * kc);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -164,7 +150,7 @@ __global__ __launch_bounds__(256) void psa_conv_dw_kernel(const T* __restrict__ 
                                                           int cin, int cout, int N, int n_citiles, int n_cotiles,
                                                           int n_splits, int n_blocks) {
   constexpr int BT = is_16bit<T>() ? 64 : 32, R = kConvTile, NT = 256;
-  using ST = Stager<T, R, BT, NT, VECOK, R, 0, 0, R>;  // channel-major only
+  using ST = Stager<T, R, BT, NT, VECOK, R>;
   constexpr int BUF = ST::NAT_ELEMS;
   __shared__ __attribute__((aligned(16))) T smem[4 * BUF];
 
@@ -193,8 +179,8 @@ __global__ __launch_bounds__(256) void psa_conv_dw_kernel(const T* __restrict__ 
   };
   auto stage = [&](int slot) {
     T* a = smem + slot * 2 * BUF;
-    sa.store(a, nullptr, tid);
-    sb.store(a + BUF, nullptr, tid);
+    sa.store(a, tid);
+    sb.store(a + BUF, tid);
   };
   if (c0 < c1) {
     load(c0);
@@ -258,10 +244,7 @@ __global__ __launch_bounds__(256) void psa_conv_dw_reduce_kernel(const float* __
 // Workgroup blk: part p = blk / (per_row * n_outer), then run n and segment
 // (256 * kCatUnroll vectors) of it; 16-byte vectors when every row length
 // and base offset allows, else single elements.
-#ifndef PSA_CAT_UNROLL
-#define PSA_CAT_UNROLL 2
-#endif
-constexpr int kCatUnroll = PSA_CAT_UNROLL;  // vectors (or elements) per thread
+constexpr int kCatUnroll = 2;  // vectors (or elements) per thread (swept 1-16)
 
 template <typename T>
 struct RowCopy {

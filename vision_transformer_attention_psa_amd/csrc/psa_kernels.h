@@ -21,8 +21,7 @@
 //                    stationary, key tiles streamed: S^T, dP^T, dS^T as
 //                    above, dQ^T += K^T dS^T.
 //   psa_bwd_fused_kernel runs both bodies in one grid (dK/dV workgroups
-//                    first); psa_bwd_dkdv_kernel / psa_bwd_dq_kernel launch
-//                    them separately (a build option, for per-pass timing).
+//                    first).
 // Every output element is written exactly once by one lane (with the
 // V-slice calls' accumulate flag: read, added to and written once): no
 // atomics, no zero-initialisation, bitwise reproducible.
@@ -42,22 +41,10 @@ namespace psa {
 
 constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before a rescale
 
-// Optional occupancy hint for the compute kernels (waves per SIMD the
-// register allocator may plan for); empty unless set at build time.
-#ifdef PSA_WAVES_PER_EU
-#define PSA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PSA_WAVES_PER_EU, PSA_WAVES_PER_EU)))
-#else
-#define PSA_OCCUPANCY
-#endif
-
-
 template <int D> struct Chunks {
   static constexpr int n = (D + 31) / 32;  // 32-wide contraction chunks
   static_assert(D % 16 == 0, "head dims must be multiples of 16");
 };
-
-template <typename T, typename S>
-__device__ __forceinline__ T* tm_of(T* base, const S&) { return base + S::NAT_ELEMS; }
 
 // Where one call's channels sit in the packed buffers.  qkv and d_packed
 // hold cs channels per slice: Q at [0, dk), K at [dk, 2dk), and this call's
@@ -78,15 +65,13 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
-  // K|V tile: K rows token-major (16-bit) for S^T, V rows channel-major for
-  // PV; with transpose reads, K rows channel-major too.
-  constexpr bool TR = tr_reads<T, kTrFwd>();
-  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, TR ? 0 : DK, TR ? 0 : DK, DK + DV>;
-  using SQ = Stager<T, DK, BM, NT, VECOK, DK, TR ? 0 : DK, 0, TR ? DK : 0>;
-  constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
-  constexpr int QE = SQ::NAT_ELEMS + SQ::TM_ELEMS;
+  // K|V tile, channel-major: K rows read as token rows for S^T, V rows as
+  // channel rows for PV.
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK>;
+  using SQ = Stager<T, DK, BM, NT, VECOK, DK>;
+  constexpr int BUF = SKV::NAT_ELEMS;
+  constexpr int QE = SQ::NAT_ELEMS;
   constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
-  constexpr int VROW = is_16bit<T>() && !TR ? 0 : DK;  // first V row in the channel-major tile
   __shared__ __attribute__((aligned(16))) T smem[SMEM];
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -101,23 +86,20 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   {
     SQ sq;
     sq.load(Qg, Qg, N, i0, tid);
-    sq.store(smem, tm_of(smem, sq), tid);
+    sq.store(smem, tid);
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < QB; ++nb)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        if constexpr (TR)
-          frag_tr<DK, false>(qf[nb][kc], smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
-        else
-          frag_tok<DK, false>(qf[nb][kc], tm_of(smem, sq), SQ::LDT, smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
+        frag_tok<DK, false>(qf[nb][kc], smem, SQ::LDN, w * QW + 16 * nb, 0, 32 * kc);
       }
     __syncthreads();
   }
 
   SKV st;
   st.load(KVg, Vg, N, 0, tid);
-  st.store(smem, tm_of(smem, st), tid);
+  st.store(smem, tid);
   __syncthreads();
 
   const Frag<T> ones = ones_frag<T>();
@@ -138,8 +120,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
     T* nat = smem + (kt & 1) * BUF;
-    const T* tm = tm_of(nat, st);
-    const T* Vt = nat + (VROW + 0) * SKV::LDN;
+    const T* Vt = nat + DK * SKV::LDN;
     if (kt + 1 < nkt) st.load(KVg, Vg, N, (kt + 1) * BN, tid);
     const int j0 = kt * BN;
 
@@ -153,10 +134,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          if constexpr (TR)
-            frag_tr<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
-          else
-            frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          frag_tok<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
@@ -220,7 +198,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
 
     if (kt + 1 < nkt) {
       T* nx = smem + ((kt + 1) & 1) * BUF;
-      st.store(nx, tm_of(nx, st), tid);
+      st.store(nx, tid);
     }
     __syncthreads();
   }
@@ -318,16 +296,13 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
 template <typename T, int DK, int DV, int KB, int NW, int BMQ>
 struct DkdvShape {
   static constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
-  // Q|dO tile: channel-major (and token-major without transpose reads).
-  // K|V stationary tile: token-major.
-  static constexpr int QG_TM = tr_reads<T, kTrDkdv>() ? 0 : DK + DV;
-  static constexpr int KV_TM = QG_TM, KV_NAT = DK + DV - QG_TM;
-  using SQG = Stager<T, DK + DV, BMQ, NT, true, DK, QG_TM, 0, DK + DV>;
-  using SKV = Stager<T, DK + DV, BNK, NT, true, DK, KV_TM, 0, KV_NAT>;
-  static constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  // Q|dO streamed tile and K|V stationary tile, both channel-major.
+  using SQG = Stager<T, DK + DV, BMQ, NT, true, DK>;
+  using SKV = Stager<T, DK + DV, BNK, NT, true, DK>;
+  static constexpr int TILE = SQG::NAT_ELEMS;
   static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 4 * BMQ * (int)sizeof(float);
   static_assert(2 * TILE * sizeof(T) % 16 == 0, "statistics must be 16-byte aligned");
-  static constexpr int KV_BYTES = (SKV::NAT_ELEMS + SKV::TM_ELEMS) * (int)sizeof(T);
+  static constexpr int KV_BYTES = SKV::NAT_ELEMS * (int)sizeof(T);
   static constexpr int SMEM = QG_BYTES > KV_BYTES ? QG_BYTES : KV_BYTES;
 };
 
@@ -342,10 +317,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BMQ % 32 == 0, "query tile must be a multiple of 32");
   static_assert(BMQ <= NT, "one statistics entry per thread");
-  constexpr bool TR = tr_reads<T, kTrDkdv>();
-  using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK, Shape::QG_TM, 0, DK + DV>;
-  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK, Shape::KV_TM, 0, Shape::KV_NAT>;
-  constexpr int TILE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK>;
+  using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK>;
+  constexpr int TILE = SQG::NAT_ELEMS;
   static_assert(TILE == Shape::TILE, "tile layout");
   T* smem = (T*)smem_raw;
   float* snl = (float*)(smem_raw + 2 * TILE * sizeof(T));  // [2][BMQ], then snd [2][BMQ]
@@ -366,25 +340,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   {
     SKV sk;
     sk.load(KVg, Vg, N, j0, tid);
-    sk.store(smem, tm_of(smem, sk), tid);
+    sk.store(smem, tid);
     __syncthreads();
-    const T* tm = tm_of(smem, sk);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int row0 = w * KW + 16 * kb;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        if constexpr (TR)
-          frag_tr<DK, false>(kf[kb][kc], smem, SKV::LDN, row0, 0, 32 * kc);
-        else
-          frag_tok<DK, false>(kf[kb][kc], tm, SKV::LDT, smem, SKV::LDN, row0, 0, 32 * kc);
+        frag_tok<DK, false>(kf[kb][kc], smem, SKV::LDN, row0, 0, 32 * kc);
       }
 #pragma unroll
       for (int cc = 0; cc < CC; ++cc) {
-        if constexpr (TR)
-          frag_tr<DV, false>(vf[kb][cc], smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
-        else
-          frag_tok<DV, false>(vf[kb][cc], tm + DK, SKV::LDT, smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
+        frag_tok<DV, false>(vf[kb][cc], smem + DK * SKV::LDN, SKV::LDN, row0, 0, 32 * cc);
       }
     }
     __syncthreads();
@@ -401,7 +368,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 
   SQG sg;
   sg.load(Qg, dOg, N, 0, tid);
-  sg.store(smem, tm_of(smem, sg), tid);
+  sg.store(smem, tid);
   for (int q = tid; q < BMQ; q += NT) {  // padding rows: P = 0
     snl[q] = q < N ? nlq[q] : kNegInf;
     snd[q] = q < N ? ndq[q] : 0.f;
@@ -412,7 +379,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // in its registers from the top of iteration qt to the end of qt + 1: a
   // prefetch distance of two tiles, at the register cost of one wherever a
   // tile needs no more than half the threads.
-  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK, Shape::QG_TM, 0, DK + DV>;
+  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK>;
   static_assert(!DEEP || BMQ <= NT / 2, "one statistics entry per thread of a half");
   const int half = tid >= NT / 2, htid = tid - half * (NT / 2);
   SQH sh;
@@ -436,7 +403,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   for (int qt = 0; qt < nqt; ++qt) {
     const int cur = qt & 1;
     const T* nat = smem + cur * TILE;   // rows: Q channels, then dO channels
-    const T* tm = tm_of(nat, sg);       // columns: Q channels, then dO channels
     const float* sl = snl + cur * BMQ;
     const float* sd = snd + cur * BMQ;
     // Prefetch a later tile (rows and its queries' statistics) into
@@ -468,20 +434,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          if constexpr (TR)
-            frag_tr<DK, true>(a, nat, SQG::LDN, 32 * c2, h, 32 * kc);
-          else
-            frag_tok<DK, true>(a, tm, SQG::LDT, nat, SQG::LDN, 32 * c2, h, 32 * kc);
+          frag_tok<DK, true>(a, nat, SQG::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(s[h][kb], a, kf[kb][kc]);
         }
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
           Frag<T> a;
-          if constexpr (TR)
-            frag_tr<DV, true>(a, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
-          else
-            frag_tok<DV, true>(a, tm + DK, SQG::LDT, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
+          frag_tok<DV, true>(a, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(dp[h][kb], a, vf[kb][cc]);
         }
@@ -522,9 +482,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
       T* nx = smem + (cur ^ 1) * TILE;
       const int lt = DEEP ? htid : tid;
       if constexpr (DEEP)
-        sh.store(nx, tm_of(nx, sg), lt);
+        sh.store(nx, lt);
       else
-        sg.store(nx, tm_of(nx, sg), lt);
+        sg.store(nx, lt);
       if (lt < BMQ) {
         snl[(cur ^ 1) * BMQ + lt] = pnl;
         snd[(cur ^ 1) * BMQ + lt] = pnd;
@@ -565,16 +525,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 template <typename T, int DK, int DV, int QB, int NW, int BN>
 struct DqShape {
   static constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
-  // K|V tile: K rows in both layouts (S^T and dQ), V rows token-major (dP^T);
-  // with transpose reads, K and V rows channel-major only.
-  static constexpr bool TR = tr_reads<T, kTrDq>();
-  static constexpr int KV_TM = TR ? 0 : DK + DV, KV_NAT = TR ? DK + DV : DK;
-  using SKV = Stager<T, DK + DV, BN, NT, true, DK, KV_TM, 0, KV_NAT>;
-  // Stationary Q|dO tile, token-major (channel-major with transpose reads).
-  static constexpr int QG_TM = TR ? 0 : DK + DV, QG_NAT = TR ? DK + DV : 0;
-  using SQG = Stager<T, DK + DV, BM, NT, true, DK, QG_TM, 0, QG_NAT>;
-  static constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
-  static constexpr int QE = SQG::NAT_ELEMS + SQG::TM_ELEMS;
+  // Streamed K|V tile and stationary Q|dO tile, both channel-major.
+  using SKV = Stager<T, DK + DV, BN, NT, true, DK>;
+  using SQG = Stager<T, DK + DV, BM, NT, true, DK>;
+  static constexpr int BUF = SKV::NAT_ELEMS;
+  static constexpr int QE = SQG::NAT_ELEMS;
   static constexpr int SMEM = (2 * BUF > QE ? 2 * BUF : QE) * (int)sizeof(T);
 };
 
@@ -587,10 +542,9 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   constexpr int QW = Shape::QW, BM = Shape::BM, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
-  constexpr bool TR = Shape::TR;
-  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK, Shape::KV_TM, 0, Shape::KV_NAT>;
-  using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK, Shape::QG_TM, 0, Shape::QG_NAT>;
-  constexpr int BUF = SKV::NAT_ELEMS + SKV::TM_ELEMS;
+  using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK>;
+  using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK>;
+  constexpr int BUF = SKV::NAT_ELEMS;
   static_assert(BUF == Shape::BUF, "tile layout");
   T* smem = (T*)smem_raw;
 
@@ -609,25 +563,18 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   {
     SQG sq;
     sq.load(Qg, dOg, N, i0, tid);
-    sq.store(smem, tm_of(smem, sq), tid);
+    sq.store(smem, tid);
     __syncthreads();
-    const T* tm = tm_of(smem, sq);
 #pragma unroll
     for (int nb = 0; nb < QB; ++nb) {
       const int row0 = w * QW + 16 * nb;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        if constexpr (TR)
-          frag_tr<DK, false>(qf[nb][kc], smem, SQG::LDN, row0, 0, 32 * kc);
-        else
-          frag_tok<DK, false>(qf[nb][kc], tm, SQG::LDT, smem, SQG::LDN, row0, 0, 32 * kc);
+        frag_tok<DK, false>(qf[nb][kc], smem, SQG::LDN, row0, 0, 32 * kc);
       }
 #pragma unroll
       for (int cc = 0; cc < CC; ++cc) {
-        if constexpr (TR)
-          frag_tr<DV, false>(gf[nb][cc], smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
-        else
-          frag_tok<DV, false>(gf[nb][cc], tm + DK, SQG::LDT, smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
+        frag_tok<DV, false>(gf[nb][cc], smem + DK * SQG::LDN, SQG::LDN, row0, 0, 32 * cc);
       }
       const int i = i0 + row0 + t;
       nl[nb] = i < N ? nlg[(size_t)bh * N + i] : kNegInf;
@@ -644,14 +591,14 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 
   SKV sk;
   sk.load(KVg, Vg, N, 0, tid);
-  sk.store(smem, tm_of(smem, sk), tid);
+  sk.store(smem, tid);
   __syncthreads();
 
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
-    const T* nat = smem + (kt & 1) * BUF;  // K channel-major (fp32, TR: K then V)
-    const T* tm = tm_of(nat, sk);          // K then V channels, token-major (not TR)
+    const T* nat = smem + (kt & 1) * BUF;  // K then V channels, channel-major
     if (kt + 1 < nkt) sk.load(KVg, Vg, N, (kt + 1) * BN, tid);
+    const int j0 = kt * BN;
 
 #pragma unroll
     for (int c2 = 0; c2 < BN / 32; ++c2) {
@@ -667,30 +614,34 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          if constexpr (TR)
-            frag_tr<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
-          else
-            frag_tok<DK, true>(a, tm, SKV::LDT, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          frag_tok<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
           Frag<T> a;
-          if constexpr (TR)
-            frag_tr<DV, true>(a, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
-          else
-            frag_tok<DV, true>(a, tm + DK, SKV::LDT, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
+          frag_tok<DV, true>(a, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }
-        // Keys past N are zero rows of K, so whatever dS^T holds for them
-        // adds nothing to dQ: no masking needed.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) dp[h][nb][r] *= fast_exp2(__builtin_fmaf(s[h][nb][r], c, nl[nb]));
         }
+      }
+      // Keys past N (zero rows of K and V): their score is 0, so P = exp(-LSE)
+      // can overflow the operand type for a query whose LSE is very negative,
+      // and inf times the zero K row would be NaN.  Their dS^T is set to 0.
+      if (j0 + 32 * c2 + 32 > N) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j0 + 32 * c2 + 8 * g + 4 * h + r >= N)
+#pragma unroll
+              for (int nb = 0; nb < QB; ++nb) dp[h][nb][r] = 0.f;
       }
       // dQ^T += K^T dS^T over this chunk's 32 keys.
       Frag<T> dsf[QB];
@@ -707,7 +658,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 
     if (kt + 1 < nkt) {
       T* nx = smem + ((kt + 1) & 1) * BUF;
-      sk.store(nx, tm_of(nx, sk), tid);
+      sk.store(nx, tid);
     }
     __syncthreads();
   }
@@ -735,31 +686,13 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 }
 
 // ========================================================= backward kernels
-template <typename T, int DK, int DV, int KB, int NW, int BMQ, bool VECOK, bool DEEP>
-__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dkdv_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
-    T* __restrict__ dpk, int N, int n_ktiles, int n_blocks, float c, float scale, const PackView pv) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM];
-  bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK, DEEP>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
-                                                     xcd_remap(block_id(), n_blocks), smem);
-}
-
-template <typename T, int DK, int DV, int QB, int NW, int BN, bool VECOK>
-__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_dq_kernel(
-    const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
-    T* __restrict__ dpk, int N, int n_qtiles, int n_blocks, float c, float scale, const PackView pv) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[DqShape<T, DK, DV, QB, NW, BN>::SMEM];
-  bwd_dq_body<T, DK, DV, QB, NW, BN, VECOK>(qkv, dO, nl, nd, dpk, N, n_qtiles, c, scale, pv,
-                                             xcd_remap(block_id(), n_blocks), smem);
-}
-
 // Both backward GEMM chains in one launch: the first n_kblocks workgroups
 // are key-stationary (dK, dV), the rest query-stationary (dQ).  The long
 // dK/dV workgroups are dispatched first and the shorter dQ ones fill the
 // machine behind them, so neither pass leaves a partly idle last wave of
 // workgroups on its own; both share one LDS allocation.
 template <typename T, int DK, int DV, int KB, int BMQ, int QB, int BN, int NW, bool VECOK, bool DEEP>
-__global__ __launch_bounds__(NW * 64) PSA_OCCUPANCY void psa_bwd_fused_kernel(
+__global__ __launch_bounds__(NW * 64) void psa_bwd_fused_kernel(
     const T* __restrict__ qkv, const T* __restrict__ dO, const float* __restrict__ nl, const float* __restrict__ nd,
     T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale,
     const PackView pv) {
