@@ -598,7 +598,6 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   for (int kt = 0; kt < nkt; ++kt) {
     const T* nat = smem + (kt & 1) * BUF;  // K then V channels, channel-major
     if (kt + 1 < nkt) sk.load(KVg, Vg, N, (kt + 1) * BN, tid);
-    const int j0 = kt * BN;
 
 #pragma unroll
     for (int c2 = 0; c2 < BN / 32; ++c2) {
@@ -625,23 +624,18 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }
+        // P is clamped to [0, 1] (the exp's output modifier, no extra
+        // instruction).  A real key has P = exp(S - LSE) <= 1 already; a key
+        // past N (zero rows of K and V) has score 0 and P = exp(-LSE), which
+        // for a query with a very negative LSE overflows the operand type,
+        // and inf times its zero K row would be NaN.  Clamped, its dS^T stays
+        // finite and meets only zeros.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
-          for (int nb = 0; nb < QB; ++nb) dp[h][nb][r] *= fast_exp2(__builtin_fmaf(s[h][nb][r], c, nl[nb]));
+          for (int nb = 0; nb < QB; ++nb)
+            dp[h][nb][r] *= __builtin_amdgcn_fmed3f(fast_exp2(__builtin_fmaf(s[h][nb][r], c, nl[nb])), 0.f, 1.f);
         }
-      }
-      // Keys past N (zero rows of K and V): their score is 0, so P = exp(-LSE)
-      // can overflow the operand type for a query whose LSE is very negative,
-      // and inf times the zero K row would be NaN.  Their dS^T is set to 0.
-      if (j0 + 32 * c2 + 32 > N) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j0 + 32 * c2 + 8 * g + 4 * h + r >= N)
-#pragma unroll
-              for (int nb = 0; nb < QB; ++nb) dp[h][nb][r] = 0.f;
       }
       // dQ^T += K^T dS^T over this chunk's 32 keys.
       Frag<T> dsf[QB];
