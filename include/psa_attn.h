@@ -105,6 +105,24 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
                  int dtype, void* stream);
 
 /*
+ * psa_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results (bitwise identical to
+ * psa_attn_bwd), but its scratch is a fixed 16 MiB device array compiled
+ * into the library, one copy per GPU, held until the process ends.  It
+ * calls no hipMalloc, hipFree or other allocating routine.
+ * Limit: B*heads*N <= 2097152 (2^21 queries, two fp32 statistics each);
+ * larger problems are refused with PSA_ERR_SHAPE before anything is
+ * enqueued.  Every call on one GPU shares that GPU's array (its contents
+ * are fully rewritten by each call before they are read), so calls that
+ * overlap in time on one GPU (concurrent streams or threads) race: order
+ * them on one stream.
+ */
+int psa_attn_bwd_noalloc(const void* qkv, const void* o, const float* lse, const void* dO,
+                         void* d_packed, int B, int heads, int N, int dk, int dv, float scale,
+                         int dtype, void* stream);
+
+/*
  * The same forward over a slice of V: rows [v0, v0 + dv) of the V section
  * of a packed buffer whose slices hold 2dk + dv_total channels.  This is the
  * call pattern of the PsaFa2Backward page, which runs one attention call per

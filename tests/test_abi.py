@@ -95,3 +95,14 @@ def test_huge_problem_rejected(lib):
     rc = binding.psa_attn_fwd(A, B_, B_ * 2, 1 << 20, 1 << 10, 1 << 20, 32, 64, 0.1,
                               binding.PSA_BF16, None)
     assert rc == 2 and "too large" in binding.psa_last_error()
+
+
+def test_noalloc_limit_rejected_before_any_device_call(lib):
+    """B*heads*N beyond the static scratch (2^21 queries) is refused with
+    PSA_ERR_SHAPE from the arguments alone (fake addresses, no GPU)."""
+    kw = dict(qkv=A, o=B_, lse=B_ * 3, dO=B_ * 2, d_packed=B_ * 4, B=64, heads=8, N=4097, dk=32,
+              dv=64, scale=0.17, dtype=binding.PSA_BF16, stream=None)
+    assert 64 * 8 * 4097 > 1 << 21
+    rc = binding.psa_attn_bwd_noalloc(**kw)
+    assert rc == 2
+    assert "static scratch limit of 2097152" in binding.psa_last_error()

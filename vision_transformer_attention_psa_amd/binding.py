@@ -20,7 +20,7 @@ STATUS = {0: "PSA_OK", 1: "PSA_ERR_NULL", 2: "PSA_ERR_SHAPE", 3: "PSA_ERR_UNSUPP
           4: "PSA_ERR_ALIGN", 5: "PSA_ERR_ALIAS", 6: "PSA_ERR_NOMEM", 7: "PSA_ERR_HIP",
           8: "PSA_ERR_DEVICE"}
 
-EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_fwd_vslice", "psa_attn_bwd_vslice", "psa_merge_fwd",
+EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_bwd_noalloc", "psa_attn_fwd_vslice", "psa_attn_bwd_vslice", "psa_merge_fwd",
            "psa_merge_bwd", "psa_qkv_conv_bwd", "psa_qkv_conv_cat_bwd",
            "psa_channel_cat_bwd", "psa_attn_supported", "psa_last_error",
            "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
@@ -51,6 +51,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.psa_attn_fwd.restype = i
     lib.psa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.psa_attn_bwd.restype = i
+    lib.psa_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.psa_attn_bwd_noalloc.restype = i
     lib.psa_attn_fwd_vslice.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     lib.psa_attn_fwd_vslice.restype = i
     lib.psa_attn_bwd_vslice.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
@@ -123,6 +125,12 @@ def psa_attn_bwd(qkv: int, o: int, lse: int, dO: int, d_packed: int, B: int, hea
                  dk: int, dv: int, scale: float, dtype: int, stream: int | None) -> int:
     """Raw call with device addresses; returns the status code."""
     return load().psa_attn_bwd(qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, scale, dtype, stream)
+
+
+def psa_attn_bwd_noalloc(qkv: int, o: int, lse: int, dO: int, d_packed: int, B: int, heads: int, N: int,
+                         dk: int, dv: int, scale: float, dtype: int, stream: int | None) -> int:
+    """Raw call with device addresses; returns the status code."""
+    return load().psa_attn_bwd_noalloc(qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, scale, dtype, stream)
 
 
 def psa_attn_fwd_vslice(qkv: int, o: int, lse: int, B: int, heads: int, N: int, dk: int, dv_total: int, v0: int,

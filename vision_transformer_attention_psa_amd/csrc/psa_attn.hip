@@ -18,6 +18,13 @@
 #include "psa_conv_kernels.h"
 #include "psa_kernels.h"
 
+// Device memory of psa_attn_bwd_noalloc, for callers that cannot allocate:
+// one fixed array per GPU (each device that runs the library holds its own
+// copy until the process ends), 16 MiB: the two fp32 statistics planes for
+// up to B*heads*N = 2^21 queries.  Host code uses only the device address
+// that hipGetSymbolAddress returns for it, never the array's name.
+static __device__ __align__(256) unsigned char scratch[size_t(16) << 20];
+
 namespace {
 
 thread_local std::string g_err;
@@ -202,6 +209,32 @@ void* scratch_for(hipStream_t st, size_t bytes) {
   return p;
 }
 
+constexpr size_t kStaticScratchBytes = sizeof(scratch);
+
+// The static array's device address on device `dev`, looked up once per
+// device (with that device current) and kept.
+struct StaticScratch {
+  std::mutex mu;
+  void* ptr[64] = {nullptr};
+};
+StaticScratch g_static;
+
+void* static_scratch(const char* fn, int dev) {
+  std::lock_guard<std::mutex> lk(g_static.mu);
+  if (g_static.ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      fail(PSA_ERR_HIP, std::string(fn) + ": hipGetSymbolAddress of the static scratch failed: " +
+                            hipGetErrorString(e));
+      return nullptr;
+    }
+    g_static.ptr[dev] = p;
+  }
+  return g_static.ptr[dev];
+}
+
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -228,9 +261,11 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, ps
   return check_launch("psa_attn_fwd launch");
 }
 
+// stats: the two fp32 statistics planes (2 * BH * N floats), or nullptr for
+// the per-stream scratch cache.
 template <typename T, int DK, int DV, class C>
 int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, void* dpk, int BH, int N,
-            float scale, psa::PackView pv, hipStream_t st) {
+            float scale, psa::PackView pv, float* stats, hipStream_t st) {
   const float c = scale * psa::kLog2e;
   const long long total = (long long)BH * N;
   constexpr int NW = C::BWD_NW;              // waves per workgroup
@@ -240,7 +275,7 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   if ((long long)BH * (nkt + nqt) > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_attn_bwd: grid too large");
   const int nkb = BH * nkt, nqb = BH * nqt;
 
-  float* stats = (float*)scratch_for(st, (size_t)total * 2 * sizeof(float));  // planes -LSE log2 e, -D
+  if (stats == nullptr) stats = (float*)scratch_for(st, (size_t)total * 2 * sizeof(float));  // -LSE log2 e, -D
   if (stats == nullptr) return PSA_ERR_NOMEM;
   const float* nl = stats;
   const float* nd = stats + total;
@@ -544,14 +579,21 @@ int attn_fwd_impl(const char* fn, const void* qkv, void* o, float* lse, int B, i
   return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": no instance");
 }
 
+// noalloc: the statistics planes live in the static device array instead
+// of the per-stream cache (no allocation at all).
 int attn_bwd_impl(const char* fn, const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed,
                   int B, int heads, int N, int dk, int dv_total, int v0, int dv, bool accum, float scale, int dtype,
-                  void* stream) {
+                  void* stream, bool noalloc = false) {
   g_err.clear();
   if (!qkv || !o || !lse || !dO || !d_packed)
     return fail(PSA_ERR_NULL, std::string(fn) + ": qkv, o, lse, dO and d_packed must be non-NULL");
   int rc = validate_common(fn, B, heads, N, dk, dv, scale, dtype);
   if (rc != PSA_OK) return rc;
+  if (noalloc && (size_t)B * heads * N * 2 * sizeof(float) > kStaticScratchBytes)
+    return fail(PSA_ERR_SHAPE, std::string(fn) + ": B*heads*N = " + std::to_string((long long)B * heads * N) +
+                                   " exceeds the static scratch limit of " +
+                                   std::to_string(kStaticScratchBytes / (2 * sizeof(float))) + " (" +
+                                   std::to_string(kStaticScratchBytes >> 20) + " MiB of statistics)");
   if ((rc = check_vslice(fn, dv_total, v0, dv)) != PSA_OK) return rc;
   if ((__int128)B * heads * (2 * (__int128)dk + dv_total) * N > ((__int128)1 << 46))
     return fail(PSA_ERR_SHAPE, std::string(fn) + ": problem too large");
@@ -569,13 +611,15 @@ int attn_bwd_impl(const char* fn, const void* qkv, const void* o, const float* l
   if ((rc = check_device(fn, &dev)) != PSA_OK) return rc;
   const Buf bufs[] = {{"qkv", rq}, {"o", ro}, {"lse", rl}, {"dO", rg}, {"d_packed", rd}};
   if ((rc = check_buffers(fn, dev, bufs, 5)) != PSA_OK) return rc;
+  float* stats = nullptr;
+  if (noalloc && (stats = (float*)static_scratch(fn, dev)) == nullptr) return PSA_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
   const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, accum ? 1 : 0};
-#define X(DT, T, K, V)                                                                                        \
-  if (dtype == DT && dk == K && dv == V)                                                                      \
-    return N <= kSmallNMaxBwd                                                                           \
-               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st) \
-               : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, st);
+#define X(DT, T, K, V)                                                                                          \
+  if (dtype == DT && dk == K && dv == V)                                                                        \
+    return N <= kSmallNMaxBwd                                                                                   \
+               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, stats, st) \
+               : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, stats, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": no instance");
@@ -711,6 +755,12 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
                  int heads, int N, int dk, int dv, float scale, int dtype, void* stream) {
   return attn_bwd_impl("psa_attn_bwd", qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, 0, dv, 0, scale, dtype,
                        stream);
+}
+
+int psa_attn_bwd_noalloc(const void* qkv, const void* o, const float* lse, const void* dO, void* d_packed, int B,
+                         int heads, int N, int dk, int dv, float scale, int dtype, void* stream) {
+  return attn_bwd_impl("psa_attn_bwd_noalloc", qkv, o, lse, dO, d_packed, B, heads, N, dk, dv, 0, dv, 0, scale,
+                       dtype, stream, true);
 }
 
 int psa_attn_fwd_vslice(const void* qkv, void* o, float* lse, int B, int heads, int N, int dk, int dv_total, int v0,
