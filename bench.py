@@ -45,8 +45,6 @@ def flops(wl) -> dict:
     return {
         "fwd": n2 * (wl.dk + wl.dv),                 # S = QK^T, O = PV
         "bwd": n2 * (3 * wl.dk + 2 * wl.dv),         # S recompute, dP, dV, dK, dQ
-        "bwd_dkdv": n2 * (2 * wl.dk + 2 * wl.dv),    # dK/dV pass: S, dP, dV, dK
-        "bwd_dq": n2 * (2 * wl.dk + wl.dv),          # dQ pass: S, dP, dQ (S, dP recomputed)
     }
 
 
@@ -242,11 +240,21 @@ def time_workload_graph(torch, wl, steps: int, warmup: int) -> dict:
         binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
     with torch.cuda.graph(gb, stream=s):
         binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
+    # the same calls K times in one graph: one graph launch per K calls
+    gfk, gbk = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gfk, stream=s):
+        for _ in range(steps):
+            binding.fwd(qkv, wl.dk, wl.dv, wl.scale, out=(o, lse))
+    with torch.cuda.graph(gbk, stream=s):
+        for _ in range(steps):
+            binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale, out=d)
     for _ in range(warmup):
         gf.replay()
         gb.replay()
+    gfk.replay()
+    gbk.replay()
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     e[0].record()
     for _ in range(steps):
         gf.replay()
@@ -254,11 +262,17 @@ def time_workload_graph(torch, wl, steps: int, warmup: int) -> dict:
     for _ in range(steps):
         gb.replay()
     e[2].record()
+    gfk.replay()
+    e[3].record()
+    gbk.replay()
+    e[4].record()
     torch.cuda.synchronize()
     fl = flops(wl)
     fwd_us = e[0].elapsed_time(e[1]) * 1e3 / steps
     bwd_us = e[1].elapsed_time(e[2]) * 1e3 / steps
-    return {"fwd_us": fwd_us, "bwd_us": bwd_us, "bwd_tflops": fl["bwd"] / (bwd_us * 1e-6) / 1e12}
+    return {"fwd_us": fwd_us, "bwd_us": bwd_us, "bwd_tflops": fl["bwd"] / (bwd_us * 1e-6) / 1e12,
+            "calls_per_graph": steps, "fwd_us_in_one_graph": e[2].elapsed_time(e[3]) * 1e3 / steps,
+            "bwd_us_in_one_graph": e[3].elapsed_time(e[4]) * 1e3 / steps}
 
 
 COLD_FLUSH_MIB = 512  # twice the 256 MB last-level cache (Infinity Cache)
@@ -455,10 +469,7 @@ def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
     us = r["kernel_avg_us"]
-    if us.get("bwd_dq") == us.get("bwd_dq"):  # split build: dK/dV and dQ launched separately
-        per_launch = {"fwd": fl["fwd"], "bwd_main": fl["bwd_dkdv"], "bwd_dq": fl["bwd_dq"]}
-    else:  # one backward launch computes dQ, dK and dV
-        per_launch = {"fwd": fl["fwd"], "bwd_main": fl["bwd"]}
+    per_launch = {"fwd": fl["fwd"], "bwd_main": fl["bwd"]}  # one backward launch computes dQ, dK and dV
     name = max(per_launch, key=lambda k: us[k])
     achieved = per_launch[name] / (us[name] * 1e-6) / 1e12
     return {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": r["peak_tflops"],
@@ -575,7 +586,9 @@ def main() -> int:
         for name in [wl.name] + [a for a in args.also.split(",") if a]:
             graph[name] = time_workload_graph(torch, inputs.WORKLOADS[name], args.steps, args.warmup)
             print(f"[bench] graph replay {name}: fwd {graph[name]['fwd_us']:.1f} us, "
-                  f"bwd {graph[name]['bwd_us']:.1f} us", file=sys.stderr, flush=True)
+                  f"bwd {graph[name]['bwd_us']:.1f} us; {args.steps} calls in one graph: fwd "
+                  f"{graph[name]['fwd_us_in_one_graph']:.1f} us, bwd {graph[name]['bwd_us_in_one_graph']:.1f} us "
+                  "per call", file=sys.stderr, flush=True)
     cold = {}
     for name in ([wl.name] + [a for a in args.also.split(",") if a]) if args.cold else []:
         cold[name] = time_workload_cold(torch, inputs.WORKLOADS[name], args.steps)

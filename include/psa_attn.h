@@ -255,8 +255,8 @@ int psa_attn_version(void);
  * bracketed by two hipEvents recorded on the launch stream; durations are
  * accumulated per kernel.  Off by default; process-wide, thread-safe.
  * Kernel slots: 0 = forward, 1 = backward preprocess (D, LSE*log2 e),
- * 2 = backward GEMM launch (dK/dV and dQ in one grid), 3 = backward dQ
- * (used only by builds with -DPSA_BWD_SPLIT=1, where slot 2 is dK/dV),
+ * 2 = backward GEMM launch (dK/dV and dQ in one grid), 3 = reserved
+ * (no kernel; always zero),
  * 4 = psa_qkv_conv_bwd / psa_qkv_conv_cat_bwd dx, 5 = their dw (with its
  * reduction), 6 = psa_channel_cat_bwd, 7 = psa_merge_fwd, 8 = psa_merge_bwd.
  * The V-slice calls use slots 0-3 like psa_attn_fwd / psa_attn_bwd.

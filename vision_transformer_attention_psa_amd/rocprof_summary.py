@@ -24,8 +24,7 @@ import sys
 from collections import defaultdict
 
 PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
-             ("psa_bwd_fused_kernel", "bwd_main"), ("psa_bwd_dkdv_kernel", "bwd_main"),
-             ("psa_bwd_dq_kernel", "bwd_dq"), ("psa_conv_dx_kernel", "conv_dx"),
+             ("psa_bwd_fused_kernel", "bwd_main"), ("psa_conv_dx_kernel", "conv_dx"),
              ("psa_conv_dw_reduce_kernel", "conv_dw_reduce"), ("psa_conv_dw_kernel", "conv_dw"),
              ("psa_rows_copy_kernel", "rows_copy"))
 
@@ -99,7 +98,7 @@ def _instance_prefixes(workload: str) -> dict:
     from vision_transformer_attention_psa_amd.inputs import WORKLOADS
     wl = WORKLOADS[workload]
     return {"fwd": f"fwd<{wl.dtype},{wl.dk},{wl.dv},", "bwd_main": f"bwd_main<{wl.dtype},{wl.dk},{wl.dv},",
-            "bwd_dq": f"bwd_dq<{wl.dtype},{wl.dk},{wl.dv},", "bwd_pre": f"bwd_pre<{wl.dtype},{wl.dv}>"}
+            "bwd_pre": f"bwd_pre<{wl.dtype},{wl.dv}>"}
 
 
 def traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: int, out_json: str,
@@ -209,6 +208,26 @@ def pmc(csvs: list, out: str, command: str, cus: int = 256, xccs: int = 8) -> No
     for r in rows:
         lines.append("| " + r[0] + " | " + " | ".join(f"{x:.1f}" if i in (0, 1, 5, 6, 7, 8, 9) else f"{x:.2f}"
                                                     for i, x in enumerate(r[1:])) + " |")
+    # Where the wave-cycles go, when the run also holds these counters.
+    att = [n for n in avg if "SQ_WAIT_INST_ANY" in avg[n] and "SQ_ACTIVE_INST_ANY" in avg[n]]
+    if att:
+        lines += ["", "Wave-cycle attribution (shares of SQ_WAVE_CYCLES): active = SQ_ACTIVE_INST_ANY (the wave "
+                  "has an instruction executing), issue wait = SQ_WAIT_INST_ANY (an instruction is ready but "
+                  "not issued: the SIMD's issue slots or the unit it needs are taken), dependency wait = "
+                  "SQ_WAIT_ANY (s_waitcnt on memory results, barriers), of which LDS issue wait = "
+                  "SQ_WAIT_INST_LDS; VALU with MFMA = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES "
+                  "(share of matrix-busy cycles in which a VALU instruction also executes).", "",
+                  "| kernel x workgroups | active % | issue wait % | dependency wait % | LDS issue wait % | "
+                  "VALU with MFMA % |", "|---|---|---|---|---|---|"]
+        for name in sorted(att, key=lambda n: -sum(dur[n].values()) / max(1, len(dur[n]))):
+            a = avg[name]
+            wc = a.get("SQ_WAVE_CYCLES", float("nan"))
+            vals_ = (100 * div(a["SQ_ACTIVE_INST_ANY"], wc), 100 * div(a["SQ_WAIT_INST_ANY"], wc),
+                     100 * div(a.get("SQ_WAIT_ANY", float("nan")), wc),
+                     100 * div(a.get("SQ_WAIT_INST_LDS", float("nan")), wc),
+                     100 * div(a.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")),
+                               a.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))))
+            lines.append(f"| {name} | " + " | ".join(f"{x:.1f}" for x in vals_) + " |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
