@@ -23,6 +23,13 @@ SHAPES = [
     (inputs.BF16, 8, 512, 1024, 1600),  # the N = 1600 block
     (inputs.BF16, 4, 512, 1536, 6400),  # the N = 6400 block
     (inputs.F16, 4, 512, 1536, 6400),
+    # large-tile dx kernels: direct-load pipeline with a partial last token
+    # tile; register-staged 256 x 256 tiles for N not a multiple of 8;
+    # register-staged 128 x 512 tiles for cin not a multiple of 256
+    (inputs.BF16, 4, 512, 1024, 6000),
+    (inputs.BF16, 4, 512, 1536, 6399),
+    (inputs.F16, 4, 384, 512, 6400),
+    (inputs.BF16, 4, 384, 512, 6397),
 ]
 
 
@@ -49,8 +56,9 @@ def test_conv_backward_parity(dtype, B, cin, cout, N):
     assert max(e.values()) <= TOL[dtype], e
 
 
-def test_conv_backward_deterministic():
-    ci = inputs.make_conv_inputs(4, 256, 512, 1000, inputs.BF16, seed=3)
+@pytest.mark.parametrize("B,cin,cout,N", [(4, 256, 512, 1000), (4, 512, 1536, 6400)])
+def test_conv_backward_deterministic(B, cin, cout, N):
+    ci = inputs.make_conv_inputs(B, cin, cout, N, inputs.BF16, seed=3)
     a, b = run_conv(ci), run_conv(ci)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 

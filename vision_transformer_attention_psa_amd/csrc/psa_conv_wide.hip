@@ -1,0 +1,343 @@
+// The qkv 1x1-convolution's dx GEMM (Conv2dBackward page, struct
+// description, in its kh = kw = 1, stride 1, g = 1 case) with large
+// workgroup tiles: dx[b][ci][n] = sum_co w[co][ci] dy[b][co][n].  Both
+// operands are read with transpose reads (w is [co][ci] and dy [co][n], the
+// contraction index the slow one in both).
+//
+// psa_conv_dx_pipe_kernel (cin a multiple of 256, N of 8): 256 x 256 tiles,
+// 8 waves, operands brought into LDS by direct global-to-LDS loads three
+// stages ahead.  psa_conv_dx_wide_kernel (the other shapes the launcher
+// takes): 128 x 128 outputs per wave, 4 waves, operands staged through
+// registers into a double-buffered LDS pair.  This file is built without the
+// option that holds MFMA accumulators in ordinary VGPRs (the attention
+// kernels, which rescale and read theirs with VALU instructions, need it):
+// the wide kernel's 256 accumulators per wave live in AGPRs.  Each epilogue
+// writes a dx row into its part of a channel concatenation (see DxParts), as
+// psa_conv_dx_kernel does.
+#include <hip/hip_runtime.h>
+
+#include "psa_conv_wide.h"
+#include "psa_conv_kernels.h"
+
+namespace psa {
+
+// Workgroup: batch b, WM x WN waves (WM * WN = 4) over a (128 WM) ci x
+// (128 WN) n tile; co in stages of 32 through a double-buffered pair of
+// channel-major tiles w[32 co][128 WM ci] and dy[32 co][128 WN n].
+template <typename T, int WM, bool VECOK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void psa_conv_dx_wide_kernel(const T* __restrict__ w, const T* __restrict__ dy, const DxParts<T> parts, int cin,
+                             int cout, int N, int n_ntiles, int n_mtiles, int n_blocks) {
+  constexpr int WN = 4 / WM, BM = 128 * WM, BN = 128 * WN, BK = 32, NT = 256;
+  static_assert(WM * WN == 4, "four waves");
+  using SA = Stager<T, BK, BM, NT, true, BK>;   // w rows co, tokens ci (row stride cin)
+  using SB = Stager<T, BK, BN, NT, VECOK, BK>;  // dy rows co, tokens n (row stride N)
+  constexpr int AE = SA::NAT_ELEMS, BE = SB::NAT_ELEMS;
+  __shared__ __attribute__((aligned(16))) T smem[2 * (AE + BE)];
+
+  const int tid = thread_id(), wv = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
+  // ci tiles innermost: the workgroups that read one dy tile run together on one XCD
+  const int blk = xcd_remap(block_id(), n_blocks);
+  const int per_b = n_ntiles * n_mtiles;
+  const int b = blk / per_b, r = blk - b * per_b;
+  const int nt = r / n_mtiles;
+  const int m0 = (r - nt * n_mtiles) * BM, n0 = nt * BN;
+  const T* dyb = dy + (size_t)b * cout * N;
+  const int wr = (wv % WM) * 128, wc = (wv / WM) * 128;  // this wave's rows (ci) and columns (n)
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  SA sa;
+  SB sb;
+  sa.load(w, w, cin, m0, tid);
+  sb.load(dyb, dyb, N, n0, tid);
+  sa.store(smem, tid);
+  sb.store(smem + AE, tid);
+  __syncthreads();
+
+  const int nk = cout / BK;
+  for (int k = 0; k < nk; ++k) {
+    const T* at = smem + (k & 1) * (AE + BE);
+    const T* bt = at + AE;
+    if (k + 1 < nk) {
+      sa.load(w + (size_t)(k + 1) * BK * cin, w, cin, m0, tid);
+      sb.load(dyb + (size_t)(k + 1) * BK * N, dyb, N, n0, tid);
+    }
+    Frag<T> fa[8], fb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) frag_tok<BK, false>(fa[i], at, SA::LDN, wr + 16 * i, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) frag_tok<BK, false>(fb[j], bt, SB::LDN, wc + 16 * j, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mma(acc[i][j], fa[i], fb[j]);
+    if (k + 1 < nk) {
+      T* nx = smem + ((k + 1) & 1) * (AE + BE);
+      sa.store(nx, tid);
+      sb.store(nx + AE, tid);
+    }
+    __syncthreads();
+  }
+
+  // acc[i][j]: row ci = m0 + wr + 16i + 4g + rr, column n = n0 + wc + 16j + t.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int ci = m0 + wr + 16 * i + 4 * g + rr;
+      T* base = parts.p[0];
+      int first = 0, ch = parts.ch[0];
+#pragma unroll
+      for (int q = 1; q < kCatMaxParts; ++q)
+        if (q < parts.n && ci >= parts.begin[q]) {
+          base = parts.p[q];
+          first = parts.begin[q];
+          ch = parts.ch[q];
+        }
+      T* row = base + ((size_t)b * ch + (ci - first)) * N;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = n0 + wc + 16 * j + t;
+        if (n < N) row[n] = from_f32<T>(acc[i][j][rr]);
+      }
+    }
+}
+
+// 16-byte direct global-to-LDS load: lane l's 16 bytes from g land at
+// lds + 16 l (lds wave-uniform, passed in M0).  Written as inline asm so that
+// the compiler does not treat the loads still in flight as pending writes to
+// every later LDS read (it would wait for all of them before the first
+// one); the kernel orders them itself with barrier_vmcnt.  The instruction
+// has no register result, so nothing the compiler allocates is written late.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(a) : "memory");
+}
+
+// Workgroup barrier once this wave's LDS reads and all but its last NV
+// vector-memory operations have completed (lgkmcnt 0, vmcnt NV; gfx9
+// s_waitcnt encoding, expcnt left at its maximum).  Unlike __syncthreads it
+// does not wait for every load in flight; the signal fences keep the
+// compiler from moving memory accesses across it.
+template <int NV>
+__device__ __forceinline__ void barrier_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((NV & 15) | (7 << 4) | ((NV >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// LDS layout of one [32 channel][RE token] 16-bit tile filled by 1 KB direct
+// loads (Q = 1024 / row bytes rows per load).  A transpose read (frag_tr's
+// lane pattern) has each half-wave read 32 bytes from each of 8 rows whose
+// channels share bits 1 and 4 and take all values of bits 0, 2, 3.  So rows
+// that share a load differ in bit 1 or 4 (never read together), and load
+// slot i starts at i * (1 KB + 32 bytes): the 8 rows of a read sit in 8
+// slots with distinct i mod 8 = h(channel), i.e. on disjoint 8-bank groups.
+template <typename T, int RE>
+struct DmaTile {
+  static constexpr int R = RE * (int)sizeof(T);  // row bytes
+  static constexpr int Q = 1024 / R;              // rows per load
+  static_assert(Q == 1 || Q == 2 || Q == 4, "rows of 256, 512 or 1024 bytes");
+  static constexpr int NI = 32 / Q;     // loads per tile
+  static constexpr int IB = 1024 + 32;  // bytes per load slot
+  static constexpr int BYTES = NI * IB;
+  // byte distance from channel c's row to channel c + 2's (c with bit 1 clear)
+  static constexpr int HI = Q >= 2 ? R : 8 * IB;
+  __device__ static __forceinline__ int h(int c) { return (c & 1) | ((c >> 1) & 6); }
+  __device__ static __forceinline__ int row_off(int c) {
+    const int b1 = (c >> 1) & 1, b4 = (c >> 4) & 1;
+    if constexpr (Q == 4) return h(c) * IB + (b1 + 2 * b4) * R;
+    else if constexpr (Q == 2) return (h(c) + 8 * b4) * IB + b1 * R;
+    else return (h(c) + 8 * b1 + 16 * b4) * IB;
+  }
+  // channel held at row position p of load slot i
+  __device__ static __forceinline__ int channel(int i, int p) {
+    const int hh = i & 7, c = (hh & 1) | ((hh & 6) << 1);
+    if constexpr (Q == 4) return c | ((p & 1) << 1) | ((p >> 1) << 4);
+    else if constexpr (Q == 2) return c | (p << 1) | ((i >> 3) << 4);
+    else return c | (((i >> 3) & 1) << 1) | ((i >> 4) << 4);
+  }
+};
+
+// A fragment (frag_tr's lane pattern) from a DmaTile: transpose reads at p
+// and p + hi (channels + 2).
+template <typename T>
+__device__ __forceinline__ void frag_lds(Frag<T>& f, const unsigned char* p, int hi) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + hi));
+  f.v = __builtin_bit_cast(typename Vec8<T>::type, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The same GEMM with a 256 ci x 256 n workgroup tile for N a multiple of 8
+// (16-byte aligned rows): 8 waves (two per SIMD), each 128 ci x 64 n (128
+// accumulators).  The operand tiles come into LDS by direct loads (DmaTile
+// layout, no staging registers) through a ring of 4 slots of 32 output
+// channels, three stages ahead of the MFMAs.  Step k, per wave: wait for its
+// own loads of stage k; one barrier (then all of stage k is in LDS and every
+// wave has finished reading stage k - 1); issue the loads of stage k + 3
+// into stage k - 1's slot; read stage k's fragments and run its 32 MFMAs.
+template <typename T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, const DxParts<T> parts, int cin,
+                             int cout, int N, int n_ntiles, int n_mtiles, int n_blocks) {
+  constexpr int NW = 8, BM = 256, BN = 256, BK = 32, JN = 4;  // JN: 16-token fragments per wave
+  using TA = DmaTile<T, BM>;
+  using TB = DmaTile<T, BN>;
+  constexpr int SB = TA::BYTES + TB::BYTES;                         // bytes per stage
+  constexpr int AI = TA::NI / NW, BI = TB::NI / NW, L = AI + BI;  // loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * SB];
+
+  const int tid = thread_id(), lane = tid & 63, g = lane >> 4, t = lane & 15, e = t >> 2;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = xcd_remap(block_id(), n_blocks);
+  const int per_b = n_ntiles * n_mtiles;
+  const int b = blk / per_b, r = blk - b * per_b;
+  const int nt = r / n_mtiles;
+  const int m0 = (r - nt * n_mtiles) * BM, n0 = nt * BN;
+  const T* dyb = dy + (size_t)b * cout * N;
+  const int wr = (wv & 1) * 128, wc = (wv >> 1) * 16 * JN;  // this wave's rows (ci) and columns (n)
+
+  // This lane's source of each direct load of a stage (element offsets):
+  // lane l fills the 16 bytes at 16 l of its load's 1 KB.
+  int a_src[AI], b_src[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int slot = wv * AI + i, p = lane / (64 / TA::Q), x = lane % (64 / TA::Q);
+    a_src[i] = TA::channel(slot, p) * cin + m0 + 8 * x;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int slot = wv * BI + i, p = lane / (64 / TB::Q), x = lane % (64 / TB::Q);
+    const int n = n0 + 8 * x;
+    b_src[i] = TB::channel(slot, p) * N + (n < N ? n : n0);  // chunks past N read a valid one; unstored columns
+  }
+  auto issue = [&](int kk, int slot) {
+    const unsigned char* sb = smem + slot * SB;
+    const T* wa = w + (size_t)kk * BK * cin;
+    const T* db = dyb + (size_t)kk * BK * N;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) lds_dma16(wa + a_src[i], sb + (wv * AI + i) * TA::IB);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) lds_dma16(db + b_src[i], sb + TA::BYTES + (wv * BI + i) * TB::IB);
+  };
+  // Fragment reads: lane (t, g) reads channel 8g + (e & 1) + 4(e >> 1) (and
+  // + 2) at tokens tok0 + 4(t & 3) .. + 3; fragment i of a wave is 32 bytes
+  // further along its rows.
+  const int ch = 8 * g + (e & 1) + 4 * (e >> 1);
+  const unsigned char* abase = smem + TA::row_off(ch) + 2 * (wr + 4 * (t & 3));
+  const unsigned char* bbase = smem + TA::BYTES + TB::row_off(ch) + 2 * (wc + 4 * (t & 3));
+
+  f32x4 acc[8][JN];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < JN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = cout / BK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 2) issue(2, 2);
+  for (int k = 0; k < nk; ++k) {
+    // this wave's loads of stage k done (those of k + 1, k + 2 may fly)
+    if (k + 2 < nk)
+      barrier_vmcnt<2 * L>();
+    else if (k + 1 < nk)
+      barrier_vmcnt<L>();
+    else
+      barrier_vmcnt<0>();
+    // every wave is past its reads of stage k - 1: reuse that slot
+    if (k + 3 < nk) issue(k + 3, (k + 3) & 3);
+    const int so = (k & 3) * SB;
+    Frag<T> fa[8], fb[JN];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) frag_lds(fb[j], bbase + so + 32 * j, TB::HI);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) frag_lds(fa[i], abase + so + 32 * i, TA::HI);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) mma(acc[i][j], fa[i], fb[j]);
+  }
+
+  // acc[i][j]: row ci = m0 + wr + 16i + 4g + rr, column n = n0 + wc + 16j + t.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int ci = m0 + wr + 16 * i + 4 * g + rr;
+      T* base = parts.p[0];
+      int first = 0, chn = parts.ch[0];
+#pragma unroll
+      for (int pq = 1; pq < kCatMaxParts; ++pq)
+        if (pq < parts.n && ci >= parts.begin[pq]) {
+          base = parts.p[pq];
+          first = parts.begin[pq];
+          chn = parts.ch[pq];
+        }
+      T* row = base + ((size_t)b * chn + (ci - first)) * N;
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        const int n = n0 + wc + 16 * j + t;
+        if (n < N) row[n] = from_f32<T>(acc[i][j][rr]);
+      }
+    }
+}
+
+namespace {
+
+template <typename T, int WM>
+void launch_wm(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N,
+               hipStream_t st) {
+  constexpr int BM = 128 * WM, BN = 128 * (4 / WM);
+  const int n_mtiles = cin / BM, n_ntiles = (N + BN - 1) / BN;
+  const int blocks = B * n_mtiles * n_ntiles;
+  if constexpr (WM == 2)
+    if (N % (16 / (int)sizeof(T)) == 0) {
+      hipLaunchKernelGGL((psa_conv_dx_pipe_kernel<T>), dim3(blocks), dim3(512), 0, st, (const T*)w, (const T*)dy,
+                         dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
+      return;
+    }
+  if (N % (16 / (int)sizeof(T)) == 0)
+    hipLaunchKernelGGL((psa_conv_dx_wide_kernel<T, WM, true>), dim3(blocks), dim3(256), 0, st, (const T*)w,
+                       (const T*)dy, dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
+  else
+    hipLaunchKernelGGL((psa_conv_dx_wide_kernel<T, WM, false>), dim3(blocks), dim3(256), 0, st, (const T*)w,
+                       (const T*)dy, dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
+}
+
+template <typename T>
+void launch(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N,
+            hipStream_t st) {
+  if (conv_dx_wide_wm(cin) == 2)
+    launch_wm<T, 2>(w, dy, dx, B, cin, cout, N, st);
+  else
+    launch_wm<T, 1>(w, dy, dx, B, cin, cout, N, st);
+}
+
+}  // namespace
+
+int conv_dx_wide_wm(int cin) { return cin % 256 == 0 ? 2 : 1; }
+
+long long conv_dx_wide_blocks(int B, int cin, int N) {
+  const int wm = conv_dx_wide_wm(cin), bm = 128 * wm, bn = 128 * (4 / wm);
+  return (long long)B * (cin / bm) * ((N + bn - 1) / bn);
+}
+
+void conv_dx_wide_launch(const void* w, const void* dy, const DxParts<bf16>& dx, int B, int cin, int cout, int N,
+                         hipStream_t st) {
+  launch<bf16>(w, dy, dx, B, cin, cout, N, st);
+}
+void conv_dx_wide_launch(const void* w, const void* dy, const DxParts<f16>& dx, int B, int cin, int cout, int N,
+                         hipStream_t st) {
+  launch<f16>(w, dy, dx, B, cin, cout, N, st);
+}
+
+}  // namespace psa
