@@ -100,6 +100,10 @@ EDGE = [
     (inputs.BF16, 64, 64, 2, 1, 384),
     (inputs.F16, 32, 64, 1, 1, 320),
     (inputs.F32, 32, 64, 1, 1, 36),
+    # rows that are not 16-byte aligned at the large-N tile shapes (funnel-shifted loads)
+    (inputs.BF16, 32, 64, 1, 2, 1599),
+    (inputs.BF16, 64, 64, 1, 1, 6399),
+    (inputs.F16, 64, 64, 1, 1, 6398),
 ]
 
 

@@ -195,6 +195,37 @@ __device__ __forceinline__ void acc_to_frag(Frag<float>& f, const f32x4& a0, con
 // aligned and spreads the 16 rows one fragment read touches over all banks.
 template <typename T> constexpr int nat_pitch(int tokens) { return tokens + 16 / (int)sizeof(T); }
 
+// Eight consecutive 16-bit elements from p, a row position that need not be
+// 16-byte aligned (rows of odd length), elements at or past
+// `avail` (>= 1) read as zero.  Two aligned 16-byte loads and a byte funnel
+// shift instead of eight 2-byte loads; the second load is issued only when
+// it holds one of the wanted elements.  Every block read is 16-byte aligned
+// and starts at or before a wanted element, so with a 16-byte aligned tensor
+// base no read leaves the tensor's pages.
+__device__ __forceinline__ u32x4 load8_funnel(const void* p, int avail) {
+  const uintptr_t a = (uintptr_t)p;
+  const u32x4* pa = (const u32x4*)(a & ~(uintptr_t)15);
+  const int sh = (int)(a & 15);                  // byte offset, even
+  const int nb = 2 * (avail < 8 ? avail : 8);    // bytes wanted
+  const u32x4 x0 = pa[0];
+  u32x4 x1 = u32x4{0u, 0u, 0u, 0u};
+  if (sh + nb > 16) x1 = pa[1];
+  const unsigned w[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  const int qd = sh >> 2, bs = sh & 3;           // whole dwords, then 0 or 2 bytes
+  unsigned d[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k)
+    d[k] = qd == 0 ? w[k] : qd == 1 ? w[k + 1] : qd == 2 ? w[k + 2] : w[k + 3];
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned v = __builtin_amdgcn_alignbyte(d[k + 1], d[k], bs);
+    const int keep = nb - 4 * k;                 // wanted bytes of dword k
+    r[k] = keep >= 4 ? v : keep == 2 ? (v & 0xffffu) : 0u;
+  }
+  return r;
+}
+
 // Global -> registers -> LDS for a tile of C channel rows x BT tokens from
 // token j0 (tokens >= N read as zero).  Rows [0, SPLIT) come from src_lo and
 // rows [SPLIT, C) from src_hi, both channel-major with row stride N.
@@ -219,9 +250,11 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   u32x4 r[PER][4];
 
   // One 16-byte chunk (8 tokens of one row) per (u, i); W bytes per load:
-  // 16 when N is a multiple of 8 (VECOK), else 8, 4 or 2 as the rows'
-  // alignment allows (masked per load; a load at token j + k*W/2 < N holds
-  // only tokens below N, as N is a multiple of W/2).
+  // 16 when N is a multiple of 8 (VECOK), else 8 or 4 as the rows' alignment
+  // allows (masked per load; a load at token j + k*W/2 < N holds only tokens
+  // below N, as N is a multiple of W/2); for odd N (W = 0) load8_funnel.
+  // (Measured at N = 6398/6399, dk = dv = 64: 4-byte loads beat the funnel's
+  // extra VALU work where they apply; 2-byte loads lose to it.)
   template <int W>
   __device__ __forceinline__ void load_w(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0, int tid) {
     constexpr int TPL = W / 2;  // tokens per load
@@ -250,10 +283,8 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
 #pragma unroll
           for (int e = 0; e < 4; ++e) r[u][i][e] = (j + TPL * e < N) ? ((const unsigned*)p)[e] : 0u;
         } else {
-          unsigned short tmp[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) tmp[e] = (j + e < N) ? ((const unsigned short*)p)[e] : (unsigned short)0;
-          __builtin_memcpy(&r[u][i], tmp, 16);
+          static_assert(W == 0, "16, 8, 4 or 0 (funnel)");
+          if (j < N) r[u][i] = load8_funnel(p, N - j);
         }
       }
     }
@@ -267,7 +298,7 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
     } else if ((N & 1) == 0) {
       load_w<4>(lo, hi, N, j0, tid);
     } else {
-      load_w<2>(lo, hi, N, j0, tid);
+      load_w<0>(lo, hi, N, j0, tid);
     }
   }
   __device__ __forceinline__ void store(T* nat, int tid) const {
