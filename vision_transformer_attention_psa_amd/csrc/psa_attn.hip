@@ -53,11 +53,6 @@ constexpr int kSmallNMax = 512;
 // to N = 256 (13.3 vs 13.9 us) and the wide ones from N = 320 (16.8 vs 17.8 us;
 // N = 400: 22.3 vs 24.2 us, N = 512: 24.2 vs 27.6 us).
 constexpr int kSmallNMaxBwd = 256;
-// Convolution dx: the large-tile kernels (one workgroup per CU) from this
-// many workgroups up.  Measured (bf16, us): 200 tiles (B 4, cin 512, cout
-// 1536, N 6400) 52 vs 74 for the 64 x 64-wave kernel; 112 tiles (8, 512,
-// 1024, 1600) 35 vs 30; 32 tiles (16, 256, 512, 400) 21 vs 14.
-constexpr long long kConvDxWideMinBlocks = 128;
 // Head dims with dk + dv > 128 ("wide heads") halve the per-wave register
 // tiles (their accumulators and stationary fragments are twice as large)
 // and the streamed LDS tiles (their rows are twice as long), so that two
@@ -324,15 +319,14 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
   const long long gx = (long long)B * n_citiles * n_ntiles;
   if (gx > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: grid too large");
   int rc;
-  // 16-bit types: the wide-tile kernel (128 x 128 outputs per wave, AGPR
-  // accumulators) when its grid covers the CUs; small problems keep more,
-  // smaller workgroups.
-  bool wide = false;
-  if constexpr (psa::is_16bit<T>()) wide = psa::conv_dx_wide_blocks(B, cin, N) >= kConvDxWideMinBlocks;
+  // 16-bit types: a large-tile kernel when the problem has enough large
+  // tiles to fill the CUs; small problems keep more, smaller workgroups.
+  psa::DxLarge large = psa::DxLarge::none;
+  if constexpr (psa::is_16bit<T>()) large = psa::conv_dx_large_kind(B, cin, N);
   {
     TimedLaunch tl(K_CONV_DX, st);
-    if (wide) {
-      if constexpr (psa::is_16bit<T>()) psa::conv_dx_wide_launch(w, dy, dx, B, cin, cout, N, st);
+    if (large != psa::DxLarge::none) {
+      if constexpr (psa::is_16bit<T>()) psa::conv_dx_large_launch(large, w, dy, dx, B, cin, cout, N, st);
     } else if (vec_ok<T>(N)) {
       hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, true>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
                          (const T*)dy, dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);

@@ -4,11 +4,11 @@
 // operands are read with transpose reads (w is [co][ci] and dy [co][n], the
 // contraction index the slow one in both).
 //
-// psa_conv_dx_pipe_kernel (cin a multiple of 256, N of 8): 256 x 256 tiles,
+// psa_conv_dx_pipe_kernel (N a multiple of 8): 256 x 256 or 128 x 256 tiles,
 // 8 waves, operands brought into LDS by direct global-to-LDS loads three
-// stages ahead.  psa_conv_dx_wide_kernel (the other shapes the launcher
-// takes): 128 x 128 outputs per wave, 4 waves, operands staged through
-// registers into a double-buffered LDS pair.  This file is built without the
+// stages ahead.  psa_conv_dx_wide_kernel (other N): 128 x 128 outputs per
+// wave, 4 waves, operands staged through registers into a double-buffered
+// LDS pair.  This file is built without the
 // option that holds MFMA accumulators in ordinary VGPRs (the attention
 // kernels, which rescale and read theirs with VALU instructions, need it):
 // the wide kernel's 256 accumulators per wave live in AGPRs.  Each epilogue
@@ -21,17 +21,18 @@
 
 namespace psa {
 
-// Workgroup: batch b, WM x WN waves (WM * WN = 4) over a (128 WM) ci x
-// (128 WN) n tile; co in stages of 32 through a double-buffered pair of
-// channel-major tiles w[32 co][128 WM ci] and dy[32 co][128 WN n].
-template <typename T, int WM, bool VECOK>
+// For rows of N not a multiple of 8 (dy staged by load widths the rows'
+// alignment allows).  Workgroup: batch b, WM x WN waves (WM * WN = 4) over a
+// (128 WM) ci x (128 WN) n tile; co in stages of 32 through a double-buffered
+// pair of channel-major tiles w[32 co][128 WM ci] and dy[32 co][128 WN n].
+template <typename T, int WM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void psa_conv_dx_wide_kernel(const T* __restrict__ w, const T* __restrict__ dy, const DxParts<T> parts, int cin,
                              int cout, int N, int n_ntiles, int n_mtiles, int n_blocks) {
   constexpr int WN = 4 / WM, BM = 128 * WM, BN = 128 * WN, BK = 32, NT = 256;
   static_assert(WM * WN == 4, "four waves");
   using SA = Stager<T, BK, BM, NT, true, BK>;   // w rows co, tokens ci (row stride cin)
-  using SB = Stager<T, BK, BN, NT, VECOK, BK>;  // dy rows co, tokens n (row stride N)
+  using SB = Stager<T, BK, BN, NT, false, BK>;  // dy rows co, tokens n (row stride N)
   constexpr int AE = SA::NAT_ELEMS, BE = SB::NAT_ELEMS;
   __shared__ __attribute__((aligned(16))) T smem[2 * (AE + BE)];
 
@@ -176,19 +177,21 @@ __device__ __forceinline__ void frag_lds(Frag<T>& f, const unsigned char* p, int
   f.v = __builtin_bit_cast(typename Vec8<T>::type, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The same GEMM with a 256 ci x 256 n workgroup tile for N a multiple of 8
-// (16-byte aligned rows): 8 waves (two per SIMD), each 128 ci x 64 n (128
-// accumulators).  The operand tiles come into LDS by direct loads (DmaTile
+// The same GEMM with a BM ci x 256 n workgroup tile (BM = 256 or 128) for N
+// a multiple of 8 (16-byte aligned rows): 8 waves (two per SIMD, 2 x 4), each
+// BM/2 ci x 64 n.  The operand tiles come into LDS by direct loads (DmaTile
 // layout, no staging registers) through a ring of 4 slots of 32 output
 // channels, three stages ahead of the MFMAs.  Step k, per wave: wait for its
 // own loads of stage k; one barrier (then all of stage k is in LDS and every
 // wave has finished reading stage k - 1); issue the loads of stage k + 3
 // into stage k - 1's slot; read stage k's fragments and run its 32 MFMAs.
-template <typename T>
+template <typename T, int BM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, const DxParts<T> parts, int cin,
                              int cout, int N, int n_ntiles, int n_mtiles, int n_blocks) {
-  constexpr int NW = 8, BM = 256, BN = 256, BK = 32, JN = 4;  // JN: 16-token fragments per wave
+  static_assert(BM == 256 || BM == 128, "ci tile");
+  constexpr int NW = 8, BN = 256, BK = 32, JN = 4;  // JN: 16-token fragments per wave
+  constexpr int IA = BM / 32;                       // 16-channel fragments per wave
   using TA = DmaTile<T, BM>;
   using TB = DmaTile<T, BN>;
   constexpr int SB = TA::BYTES + TB::BYTES;                         // bytes per stage
@@ -203,7 +206,7 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
   const int nt = r / n_mtiles;
   const int m0 = (r - nt * n_mtiles) * BM, n0 = nt * BN;
   const T* dyb = dy + (size_t)b * cout * N;
-  const int wr = (wv & 1) * 128, wc = (wv >> 1) * 16 * JN;  // this wave's rows (ci) and columns (n)
+  const int wr = (wv & 1) * (BM / 2), wc = (wv >> 1) * 16 * JN;  // this wave's rows (ci) and columns (n)
 
   // This lane's source of each direct load of a stage (element offsets):
   // lane l fills the 16 bytes at 16 l of its load's 1 KB.
@@ -235,9 +238,9 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
   const unsigned char* abase = smem + TA::row_off(ch) + 2 * (wr + 4 * (t & 3));
   const unsigned char* bbase = smem + TA::BYTES + TB::row_off(ch) + 2 * (wc + 4 * (t & 3));
 
-  f32x4 acc[8][JN];
+  f32x4 acc[IA][JN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < IA; ++i)
 #pragma unroll
     for (int j = 0; j < JN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -256,20 +259,20 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
     // every wave is past its reads of stage k - 1: reuse that slot
     if (k + 3 < nk) issue(k + 3, (k + 3) & 3);
     const int so = (k & 3) * SB;
-    Frag<T> fa[8], fb[JN];
+    Frag<T> fa[IA], fb[JN];
 #pragma unroll
     for (int j = 0; j < JN; ++j) frag_lds(fb[j], bbase + so + 32 * j, TB::HI);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) frag_lds(fa[i], abase + so + 32 * i, TA::HI);
+    for (int i = 0; i < IA; ++i) frag_lds(fa[i], abase + so + 32 * i, TA::HI);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < IA; ++i)
 #pragma unroll
       for (int j = 0; j < JN; ++j) mma(acc[i][j], fa[i], fb[j]);
   }
 
   // acc[i][j]: row ci = m0 + wr + 16i + 4g + rr, column n = n0 + wc + 16j + t.
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < IA; ++i)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int ci = m0 + wr + 16 * i + 4 * g + rr;
@@ -293,51 +296,66 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
 
 namespace {
 
+// Large-tile kernels need this many workgroups (one per CU) to pay off.
+// Measured (bf16, us, against the 64 x 64-wave kernel): B 4, cin 512, cout
+// 1536, N 6400: 256 x 256 pipeline (200 tiles) 49-52, 128 x 256 (400) 54,
+// small tiles 72-74; B 8, cin 512, cout 1024, N 1600: 256 x 256 (112 tiles)
+// 35, 128 x 256 (224) 24, small tiles 30; register-staged 256 x 256 at
+// N = 6399 (200 tiles) 181-203 vs 277.
+constexpr long long kPipe256MinBlocks = 192;
+constexpr long long kPipe128MinBlocks = 128;
+constexpr long long kStagedMinBlocks = 128;
+
+long long tiles(int B, int cin, int N, int bm, int bn) {
+  return (long long)B * (cin / bm) * ((N + bn - 1) / bn);
+}
+
+template <typename T, int BM>
+void pipe(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N, hipStream_t st) {
+  const int n_mtiles = cin / BM, n_ntiles = (N + 255) / 256, blocks = B * n_mtiles * n_ntiles;
+  hipLaunchKernelGGL((psa_conv_dx_pipe_kernel<T, BM>), dim3(blocks), dim3(512), 0, st, (const T*)w, (const T*)dy, dx,
+                     cin, cout, N, n_ntiles, n_mtiles, blocks);
+}
+
 template <typename T, int WM>
-void launch_wm(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N,
-               hipStream_t st) {
+void staged(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N, hipStream_t st) {
   constexpr int BM = 128 * WM, BN = 128 * (4 / WM);
-  const int n_mtiles = cin / BM, n_ntiles = (N + BN - 1) / BN;
-  const int blocks = B * n_mtiles * n_ntiles;
-  if constexpr (WM == 2)
-    if (N % (16 / (int)sizeof(T)) == 0) {
-      hipLaunchKernelGGL((psa_conv_dx_pipe_kernel<T>), dim3(blocks), dim3(512), 0, st, (const T*)w, (const T*)dy,
-                         dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
-      return;
-    }
-  if (N % (16 / (int)sizeof(T)) == 0)
-    hipLaunchKernelGGL((psa_conv_dx_wide_kernel<T, WM, true>), dim3(blocks), dim3(256), 0, st, (const T*)w,
-                       (const T*)dy, dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
-  else
-    hipLaunchKernelGGL((psa_conv_dx_wide_kernel<T, WM, false>), dim3(blocks), dim3(256), 0, st, (const T*)w,
-                       (const T*)dy, dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
+  const int n_mtiles = cin / BM, n_ntiles = (N + BN - 1) / BN, blocks = B * n_mtiles * n_ntiles;
+  hipLaunchKernelGGL((psa_conv_dx_wide_kernel<T, WM>), dim3(blocks), dim3(256), 0, st, (const T*)w, (const T*)dy,
+                     dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
 }
 
 template <typename T>
-void launch(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N,
+void launch(DxLarge kind, const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N,
             hipStream_t st) {
-  if (conv_dx_wide_wm(cin) == 2)
-    launch_wm<T, 2>(w, dy, dx, B, cin, cout, N, st);
-  else
-    launch_wm<T, 1>(w, dy, dx, B, cin, cout, N, st);
+  switch (kind) {
+    case DxLarge::pipe256: pipe<T, 256>(w, dy, dx, B, cin, cout, N, st); break;
+    case DxLarge::pipe128: pipe<T, 128>(w, dy, dx, B, cin, cout, N, st); break;
+    case DxLarge::staged256: staged<T, 2>(w, dy, dx, B, cin, cout, N, st); break;
+    case DxLarge::staged128: staged<T, 1>(w, dy, dx, B, cin, cout, N, st); break;
+    case DxLarge::none: break;
+  }
 }
 
 }  // namespace
 
-int conv_dx_wide_wm(int cin) { return cin % 256 == 0 ? 2 : 1; }
-
-long long conv_dx_wide_blocks(int B, int cin, int N) {
-  const int wm = conv_dx_wide_wm(cin), bm = 128 * wm, bn = 128 * (4 / wm);
-  return (long long)B * (cin / bm) * ((N + bn - 1) / bn);
+DxLarge conv_dx_large_kind(int B, int cin, int N) {
+  if (N % 8 == 0) {  // 16-byte rows of a 16-bit type
+    if (cin % 256 == 0 && tiles(B, cin, N, 256, 256) >= kPipe256MinBlocks) return DxLarge::pipe256;
+    if (tiles(B, cin, N, 128, 256) >= kPipe128MinBlocks) return DxLarge::pipe128;
+    return DxLarge::none;
+  }
+  if (cin % 256 == 0) return tiles(B, cin, N, 256, 256) >= kStagedMinBlocks ? DxLarge::staged256 : DxLarge::none;
+  return tiles(B, cin, N, 128, 512) >= kStagedMinBlocks ? DxLarge::staged128 : DxLarge::none;
 }
 
-void conv_dx_wide_launch(const void* w, const void* dy, const DxParts<bf16>& dx, int B, int cin, int cout, int N,
-                         hipStream_t st) {
-  launch<bf16>(w, dy, dx, B, cin, cout, N, st);
+void conv_dx_large_launch(DxLarge kind, const void* w, const void* dy, const DxParts<bf16>& dx, int B, int cin,
+                          int cout, int N, hipStream_t st) {
+  launch<bf16>(kind, w, dy, dx, B, cin, cout, N, st);
 }
-void conv_dx_wide_launch(const void* w, const void* dy, const DxParts<f16>& dx, int B, int cin, int cout, int N,
-                         hipStream_t st) {
-  launch<f16>(w, dy, dx, B, cin, cout, N, st);
+void conv_dx_large_launch(DxLarge kind, const void* w, const void* dy, const DxParts<f16>& dx, int B, int cin,
+                          int cout, int N, hipStream_t st) {
+  launch<f16>(kind, w, dy, dx, B, cin, cout, N, st);
 }
 
 }  // namespace psa
