@@ -465,6 +465,48 @@ def time_lohi(torch, wl, steps: int, warmup: int) -> dict | None:
     return {"halves": [h, wl.dv - h], "fwd_us": timed(fwd), "bwd_us": timed(bwd)}
 
 
+def time_torch_sdpa(torch, wl, x, steps: int, warmup: int) -> dict | None:
+    """For context only: torch's fused attention (scaled_dot_product_attention
+    restricted to one backend at a time, so that nothing falls back to the
+    unfused math path) on the same inputs, converted to its token-major
+    [B, heads, N, d] layout outside the timed region.  Needs dk == dv (torch
+    has no fused kernel otherwise).  Backward = (forward + backward) -
+    forward, both timed with hipEvents over `steps` calls."""
+    from vision_transformer_attention_psa_amd import inputs
+    if wl.dk != wl.dv or wl.dtype == inputs.F32:
+        return None
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    qkv, dO = x
+    tok = lambda t: t.transpose(-1, -2).contiguous()
+    q, k, v = (tok(qkv[:, :, a:a + wl.dk]) for a in (0, wl.dk, 2 * wl.dk))
+    go = tok(dO)
+    res = {"layout": "token-major [B, heads, N, d]", "note": "platform library, for context; not this library"}
+    for backend in (SDPBackend.EFFICIENT_ATTENTION, SDPBackend.FLASH_ATTENTION):
+        try:
+            with sdpa_kernel([backend]):
+                qq, kk, vv = (t.detach().requires_grad_() for t in (q, k, v))
+                fwd = lambda: torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=wl.scale)
+
+                def both():
+                    fwd().backward(go)
+                us = {}
+                for name, fn in (("fwd", fwd), ("fwd_bwd", both)):
+                    for _ in range(warmup):
+                        fn()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    e0.record()
+                    for _ in range(steps):
+                        fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us[name] = e0.elapsed_time(e1) * 1e3 / steps
+                res[backend.name.lower()] = {"fwd_us": us["fwd"], "bwd_us": us["fwd_bwd"] - us["fwd"]}
+        except Exception as e:  # the backend may be unavailable on a given build
+            res[backend.name.lower()] = {"unavailable": f"{type(e).__name__}: {str(e)[:160]}"}
+    return res
+
+
 def roofline(wl, r: dict, traffic: dict | None) -> dict:
     """Dominant kernel of the step (largest average duration)."""
     fl = flops(wl)
@@ -545,6 +587,8 @@ def main() -> int:
     ap.add_argument("--also", default=",".join(ALSO), help="comma list of extra workloads ('' for none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--graph", type=int, default=1, help="also time HIP-graph replay of the step (1/0)")
+    ap.add_argument("--sdpa", type=int, default=1,
+                    help="also time torch's fused attention on the headline inputs, for context (1/0)")
     ap.add_argument("--cold", type=int, default=0,
                     help="also time each call after overwriting 512 MiB (cold caches; 1/0). Off by default "
                          "so that a profile of the default command holds warm calls only")
@@ -608,6 +652,13 @@ def main() -> int:
         print(f"[bench] lo/hi two-call pattern (halves {lohi['halves']}): fwd {lohi['fwd_us']:.1f} us, "
               f"bwd {lohi['bwd_us']:.1f} us (one call: fwd {r['fwd_us']:.1f}, bwd {r['bwd_us']:.1f})",
               file=sys.stderr, flush=True)
+    sdpa = None
+    if args.sdpa:
+        sdpa = time_torch_sdpa(torch, wl, device_inputs(torch, r["inputs"])[:2], args.steps, args.warmup)
+        if sdpa:
+            print("[bench] torch fused attention (context) " + ", ".join(
+                f"{k}: fwd {v['fwd_us']:.1f} us, bwd {v['bwd_us']:.1f} us" if "fwd_us" in v else f"{k}: unavailable"
+                for k, v in sdpa.items() if isinstance(v, dict)), file=sys.stderr, flush=True)
     traffic = load_traffic(wl.name)
     cpu = None
     if args.cpu_budget > 0:
@@ -649,6 +700,7 @@ def main() -> int:
         "qkv_conv_bwd": conv,
         "channel_cat_bwd": cat,
         "lo_hi_two_call": lohi,
+        "torch_sdpa_reference": sdpa,
     }
     print(json.dumps(out), flush=True)
     return 0
