@@ -89,6 +89,7 @@ FOLD_CASES = [
     (inputs.F16, 1, 256, 256, 400, [200, 56]),
     (inputs.BF16, 16, 256, 512, 400, [128, 128]),
     (inputs.BF16, 4, 512, 1536, 6400, [256, 256]),  # the N = 6400 block, input = cat of two halves
+    (inputs.BF16, 4, 512, 1536, 6399, [128, 256, 128]),  # zero-padded rows into the large-tile pipeline
 ]
 
 

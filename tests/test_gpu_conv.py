@@ -23,9 +23,9 @@ SHAPES = [
     (inputs.BF16, 8, 512, 1024, 1600),  # the N = 1600 block
     (inputs.BF16, 4, 512, 1536, 6400),  # the N = 6400 block
     (inputs.F16, 4, 512, 1536, 6400),
-    # large-tile dx kernels: direct-load pipeline with a partial last token
-    # tile; register-staged 256 x 256 tiles for N not a multiple of 8;
-    # register-staged 128 x 512 tiles for cin not a multiple of 256
+    # large-tile dx pipeline: a partial last token tile; N not a multiple
+    # of 8 (rows staged into zero-padded copies, remainders 7 and 5); cin
+    # not a multiple of 256 (128 x 256 tiles)
     (inputs.BF16, 4, 512, 1024, 6000),
     (inputs.BF16, 4, 512, 1536, 6399),
     (inputs.F16, 4, 384, 512, 6400),

@@ -100,7 +100,12 @@ EDGE = [
     (inputs.BF16, 64, 64, 2, 1, 384),
     (inputs.F16, 32, 64, 1, 1, 320),
     (inputs.F32, 32, 64, 1, 1, 36),
-    # rows that are not 16-byte aligned at the large-N tile shapes (funnel-shifted loads)
+    # rows that are not 16-byte aligned: below the staging length the kernels load them
+    # with 8-, 4- or 2-byte loads or funnel shifts (N % 8 = 4, 6, odd); from it on they
+    # are staged into zero-padded rows, also at the large-N tile shapes
+    (inputs.F16, 32, 64, 2, 1, 60),
+    (inputs.BF16, 32, 64, 1, 1, 94),
+    (inputs.BF16, 64, 64, 1, 2, 63),
     (inputs.BF16, 32, 64, 1, 2, 1599),
     (inputs.BF16, 64, 64, 1, 1, 6399),
     (inputs.F16, 64, 64, 1, 1, 6398),

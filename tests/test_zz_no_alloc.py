@@ -46,6 +46,25 @@ def test_noalloc_matches_allocating_backward_twice():
         assert orc.max_rel_err(g, r) <= TOL[wl.dtype]
 
 
+def test_noalloc_unpadded_rows_match_padded():
+    """At N = 1599 the allocating backward stages its inputs into rows padded
+    to a multiple of 8; the allocation-free one reads the ragged rows as they
+    are.  Same kernels otherwise: bitwise equal."""
+    t = torch()
+    wl = inputs.WORKLOADS["midres_n1600_bf16"].with_(B=1, heads=2, H=41, W=39, seed=43)  # N = 1599
+    x = inputs.make_inputs(wl)
+    qkv, dO = device_inputs(x)
+    o, lse = binding.fwd(qkv, wl.dk, wl.dv, wl.scale)
+    ref = binding.bwd(qkv, o, lse, dO, wl.dk, wl.dv, wl.scale)
+    got = _noalloc(qkv, o, lse, dO, wl)
+    t.cuda.synchronize()
+    assert t.equal(got, ref)
+    sl = inputs.sample_slices(wl, 1)
+    d_ref = orc.backward(x.qkv, to_host(o), to_host(lse), x.dO, wl.dk, wl.dv, wl.scale, slices=sl)
+    g = to_host(got).reshape(wl.BH, wl.channels, wl.N)[sl]
+    assert orc.max_rel_err(g, d_ref.reshape(wl.BH, wl.channels, wl.N)[sl]) <= TOL[wl.dtype]
+
+
 def test_noalloc_refuses_beyond_its_limit():
     t = torch()
     qkv = t.zeros((1, 1, 128, 8), dtype=t.bfloat16, device="cuda")

@@ -244,6 +244,40 @@ int check_launch(const char* what) {
 
 template <typename T> constexpr bool vec_ok(int N) { return N % (16 / (int)sizeof(T)) == 0; }
 
+// Inputs whose rows (N tokens of a 16-bit type) are not a multiple of 8 are
+// staged once into zero-padded rows of N rounded up to 8, so that the
+// kernels load them with aligned 16-byte loads.  Measured (bf16, whole
+// calls, about 32 K tokens x 8 heads): attention gains from N = 127 on
+// (fwd 54 -> 46 us; N = 1021: 212 -> 120, bwd 583 -> 302) and loses below
+// (N = 61: fwd 39.5 -> 43, the copy's launch and traffic outweigh the
+// narrower loads), so attention pads from this length on; the convolution
+// gradient (B x 512 x 1536 at 25.6 K tokens) gains at every N
+// (N = 61: 975 -> 312 us, N = 6399: 580 -> 199) and always pads.
+constexpr int kAttnPadMinN = 96;
+
+// Row stride for a call's inputs: N, or N rounded up to 8 when N >= min_n.
+int input_ld(int dtype, int N, long long rows, int min_n) {
+  if (dtype == PSA_F32 || N % 8 == 0 || N < min_n) return N;
+  const int ld = (N + 7) & ~7;
+  if (rows * (ld / 8) / 256 >= INT32_MAX) return N;  // the copy's grid
+  return ld;
+}
+
+// dst[r][0, ld) = src[r][0, n) then zeros, for `rows` rows.
+int pad_rows(int dtype, const void* src, void* dst, long long rows, int n, int ld, hipStream_t st) {
+  const long long chunks = rows * (ld / 8);
+  const dim3 g((unsigned)((chunks + 255) / 256)), b(256);
+  if (dtype == PSA_BF16)
+    hipLaunchKernelGGL((psa::psa_pad_rows_kernel<psa::bf16>), g, b, 0, st, (const psa::bf16*)src, (psa::bf16*)dst,
+                       rows, n, ld);
+  else
+    hipLaunchKernelGGL((psa::psa_pad_rows_kernel<psa::f16>), g, b, 0, st, (const psa::f16*)src, (psa::f16*)dst, rows,
+                       n, ld);
+  return check_launch("psa_attn input staging launch");
+}
+
+constexpr size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 template <typename T, int DK, int DV, class C>
 int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, psa::PackView pv, hipStream_t st) {
   constexpr int BM = C::FWD_NW * 16 * C::FWD_QB;
@@ -253,7 +287,7 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, ps
   const float c = scale * psa::kLog2e;
   const dim3 g((unsigned)grid), b(C::FWD_NW * 64);
   TimedLaunch tl(K_FWD, st);
-  if (vec_ok<T>(N))
+  if (vec_ok<T>(pv.ld))
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true, C::FWD_OCC>), g, b, 0, st,
                        (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   else
@@ -284,13 +318,13 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   int rc;
   {
     TimedLaunch tl(K_PRE, st);
-    if (vec_ok<T>(N)) {  // 16-byte token groups x 8 channel groups, 256 lanes per 256 x 16 bytes of tokens
-      const long long lanes = total / (16 / (long long)sizeof(T)) * 8;
+    if (vec_ok<T>(pv.ld)) {  // 16-byte token groups x 8 channel groups, 256 lanes per 256 x 16 bytes of tokens
+      const long long lanes = (long long)BH * (pv.ld / (16 / (int)sizeof(T))) * 8;
       hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV, true>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0,
-                         st, (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+                         st, (const T*)o, (const T*)dO, lse, stats, N, pv.ld, (int)total);
     } else {
       hipLaunchKernelGGL((psa::psa_bwd_pre_kernel<T, DV, false>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                         st, (const T*)o, (const T*)dO, lse, stats, N, (int)total);
+                         st, (const T*)o, (const T*)dO, lse, stats, N, pv.ld, (int)total);
     }
     rc = check_launch("psa_attn_bwd preprocess launch");
   }
@@ -298,7 +332,7 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   {
     TimedLaunch tl(K_MAIN, st);
     const dim3 grid((unsigned)(nkb + nqb)), block(NW * 64);
-    if (vec_ok<T>(N))
+    if (vec_ok<T>(pv.ld))
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, true, C::DKDV_DEEP>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);
@@ -313,36 +347,21 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
 
 template <typename T>
 int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxParts<T>& dx, void* dw, int B, int cin,
-                 int cout, int N, hipStream_t st) {
+                 int cout, int N, int dtype, hipStream_t st) {
   constexpr int R = psa::kConvTile;
   const int n_ntiles = (N + R - 1) / R, n_citiles = cin / R, n_cotiles = cout / R;
   const long long gx = (long long)B * n_citiles * n_ntiles;
   if (gx > INT32_MAX) return fail(PSA_ERR_SHAPE, "psa_qkv_conv_bwd: grid too large");
-  int rc;
-  // 16-bit types: a large-tile kernel when the problem has enough large
-  // tiles to fill the CUs; small problems keep more, smaller workgroups.
-  psa::DxLarge large = psa::DxLarge::none;
-  if constexpr (psa::is_16bit<T>()) large = psa::conv_dx_large_kind(B, cin, N);
-  {
-    TimedLaunch tl(K_CONV_DX, st);
-    if (large != psa::DxLarge::none) {
-      if constexpr (psa::is_16bit<T>()) psa::conv_dx_large_launch(large, w, dy, dx, B, cin, cout, N, st);
-    } else if (vec_ok<T>(N)) {
-      hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, true>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
-                         (const T*)dy, dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
-    } else {
-      hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, false>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
-                         (const T*)dy, dx, cin, cout, N, n_ntiles, n_citiles, (int)gx);
-    }
-    rc = check_launch("psa_qkv_conv_bwd dx launch");
-  }
-  if (rc != PSA_OK) return rc;
+  // Rows of x and dy in padded copies (see kAttnPadMinN): dx reads dy with
+  // row stride ld and writes rows of N; dw sums over all ld tokens, the zero
+  // columns adding nothing.
+  const int ld = input_ld(dtype, N, (long long)B * (cin + cout), 1);
   // dw: the (b, token chunk) sum is split into S ranges so that tiles x S
   // fills the two workgroups per CU that its 74 KB of LDS allow, rounded
   // down: one more workgroup than the CUs hold would cost a second round.
   // Each range keeps >= 4 chunks.
   constexpr int BT = psa::is_16bit<T>() ? 64 : 32;
-  const long long nchunk = (long long)B * ((N + BT - 1) / BT);
+  const long long nchunk = (long long)B * ((ld + BT - 1) / BT);
   const int tiles = n_citiles * n_cotiles;
   int cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -350,19 +369,50 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
   long long S = (2LL * cus) / tiles;
   S = std::min<long long>(S, std::max<long long>(1, nchunk / 4));
   S = std::max<long long>(1, std::min<long long>(S, 64));
+  // one scratch buffer: dw's fp32 partials, then the padded x and dy
+  const size_t pb = S > 1 ? round256((size_t)S * cout * cin * sizeof(float)) : 0;
+  const size_t xb = ld != N ? round256((size_t)B * cin * ld * sizeof(T)) : 0;
+  const size_t yb = ld != N ? round256((size_t)B * cout * ld * sizeof(T)) : 0;
   float* part = nullptr;
-  if (S > 1) {
-    part = (float*)scratch_for(st, (size_t)S * cout * cin * sizeof(float));
-    if (part == nullptr) return PSA_ERR_NOMEM;
+  int rc;
+  if (pb + xb + yb > 0) {
+    unsigned char* base = (unsigned char*)scratch_for(st, pb + xb + yb);
+    if (base == nullptr) return fail(PSA_ERR_NOMEM, std::string("psa_qkv_conv_bwd: ") + g_err);
+    if (S > 1) part = (float*)base;
+    if (ld != N) {
+      if ((rc = pad_rows(dtype, x, base + pb, (long long)B * cin, N, ld, st)) != PSA_OK ||
+          (rc = pad_rows(dtype, dy, base + pb + xb, (long long)B * cout, N, ld, st)) != PSA_OK)
+        return rc;
+      x = base + pb;
+      dy = base + pb + xb;
+    }
   }
+  // 16-bit types: a large-tile kernel when the problem has enough large
+  // tiles to fill the CUs; small problems keep more, smaller workgroups.
+  psa::DxLarge large = psa::DxLarge::none;
+  if constexpr (psa::is_16bit<T>()) large = psa::conv_dx_large_kind(B, cin, N, ld);
+  {
+    TimedLaunch tl(K_CONV_DX, st);
+    if (large != psa::DxLarge::none) {
+      if constexpr (psa::is_16bit<T>()) psa::conv_dx_large_launch(large, w, dy, dx, B, cin, cout, N, ld, st);
+    } else if (vec_ok<T>(ld)) {
+      hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, true>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
+                         (const T*)dy, dx, cin, cout, N, ld, n_ntiles, n_citiles, (int)gx);
+    } else {
+      hipLaunchKernelGGL((psa::psa_conv_dx_kernel<T, false>), dim3((unsigned)gx), dim3(256), 0, st, (const T*)w,
+                         (const T*)dy, dx, cin, cout, N, ld, n_ntiles, n_citiles, (int)gx);
+    }
+    rc = check_launch("psa_qkv_conv_bwd dx launch");
+  }
+  if (rc != PSA_OK) return rc;
   TimedLaunch tl(K_CONV_DW, st);
   const int gw = (int)(tiles * S);
-  if (vec_ok<T>(N))
+  if (vec_ok<T>(ld))
     hipLaunchKernelGGL((psa::psa_conv_dw_kernel<T, true>), dim3((unsigned)gw), dim3(256), 0, st, (const T*)x,
-                       (const T*)dy, (T*)dw, part, B, cin, cout, N, n_citiles, n_cotiles, (int)S, gw);
+                       (const T*)dy, (T*)dw, part, B, cin, cout, ld, n_citiles, n_cotiles, (int)S, gw);
   else
     hipLaunchKernelGGL((psa::psa_conv_dw_kernel<T, false>), dim3((unsigned)gw), dim3(256), 0, st, (const T*)x,
-                       (const T*)dy, (T*)dw, part, B, cin, cout, N, n_citiles, n_cotiles, (int)S, gw);
+                       (const T*)dy, (T*)dw, part, B, cin, cout, ld, n_citiles, n_cotiles, (int)S, gw);
   rc = check_launch("psa_qkv_conv_bwd dw launch");
   if (rc == PSA_OK && S > 1) {
     const long long n = (long long)cout * cin;
@@ -577,11 +627,20 @@ int attn_fwd_impl(const char* fn, const void* qkv, void* o, float* lse, int B, i
   const Buf bufs[] = {{"qkv", rq}, {"o", ro}, {"lse", rl}};
   if ((rc = check_buffers(fn, dev, bufs, 3)) != PSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, 0};
+  const long long rows = (long long)BH * (2 * dk + dv_total);
+  const int ld = input_ld(dtype, N, rows, kAttnPadMinN);
+  const void* qin = qkv;
+  if (ld != N) {
+    void* q = scratch_for(st, (size_t)rows * ld * e);
+    if (q == nullptr) return fail(PSA_ERR_NOMEM, std::string(fn) + ": " + g_err);
+    if ((rc = pad_rows(dtype, qkv, q, rows, N, ld, st)) != PSA_OK) return rc;
+    qin = q;
+  }
+  const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, 0, ld};
 #define X(DT, T, K, V)                                                                                   \
   if (dtype == DT && dk == K && dv == V)                                                                 \
-    return N <= kSmallNMax ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st) \
-                                : run_fwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, (int)BH, N, scale, pv, st);
+    return N <= kSmallNMax ? run_fwd<T, K, V, TilesNarrow<T, K, V>>(qin, o, lse, (int)BH, N, scale, pv, st) \
+                                : run_fwd<T, K, V, TilesWide<T, K, V>>(qin, o, lse, (int)BH, N, scale, pv, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": no instance");
@@ -622,12 +681,29 @@ int attn_bwd_impl(const char* fn, const void* qkv, const void* o, const float* l
   float* stats = nullptr;
   if (noalloc && (stats = (float*)static_scratch(fn, dev)) == nullptr) return PSA_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
-  const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, accum ? 1 : 0};
+  const long long qrows = (long long)BH * (2 * dk + dv_total), grows = (long long)BH * dv;
+  const int ld = noalloc ? N : input_ld(dtype, N, qrows, kAttnPadMinN);
+  const void *qin = qkv, *oin = o, *gin = dO;
+  if (ld != N) {  // statistics, then the three inputs in padded rows, in one scratch buffer
+    const size_t sb = round256((size_t)BH * N * 2 * sizeof(float)), qb = round256((size_t)qrows * ld * e),
+                 gb = round256((size_t)grows * ld * e);
+    unsigned char* base = (unsigned char*)scratch_for(st, sb + qb + 2 * gb);
+    if (base == nullptr) return fail(PSA_ERR_NOMEM, std::string(fn) + ": " + g_err);
+    stats = (float*)base;
+    qin = base + sb;
+    oin = base + sb + qb;
+    gin = base + sb + qb + gb;
+    if ((rc = pad_rows(dtype, qkv, (void*)qin, qrows, N, ld, st)) != PSA_OK ||
+        (rc = pad_rows(dtype, o, (void*)oin, grows, N, ld, st)) != PSA_OK ||
+        (rc = pad_rows(dtype, dO, (void*)gin, grows, N, ld, st)) != PSA_OK)
+      return rc;
+  }
+  const psa::PackView pv{2 * dk + dv_total, 2 * dk + v0, accum ? 1 : 0, ld};
 #define X(DT, T, K, V)                                                                                          \
   if (dtype == DT && dk == K && dv == V)                                                                        \
     return N <= kSmallNMaxBwd                                                                                   \
-               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, stats, st) \
-               : run_bwd<T, K, V, TilesWide<T, K, V>>(qkv, o, lse, dO, d_packed, (int)BH, N, scale, pv, stats, st);
+               ? run_bwd<T, K, V, TilesNarrow<T, K, V>>(qin, oin, lse, gin, d_packed, (int)BH, N, scale, pv, stats, st) \
+               : run_bwd<T, K, V, TilesWide<T, K, V>>(qin, oin, lse, gin, d_packed, (int)BH, N, scale, pv, stats, st);
   PSA_INSTANCES(X)
 #undef X
   return fail(PSA_ERR_UNSUPPORTED, std::string(fn) + ": no instance");
@@ -694,7 +770,7 @@ int conv_bwd_impl(const char* fn, const void* x, const void* w, const void* dy, 
       if (k < n_parts) first += part_channels[k];
     }
     parts.n = n_parts;
-    return run_conv_bwd<T>(x, w, dy, parts, dw, B, cin, cout, N, st);
+    return run_conv_bwd<T>(x, w, dy, parts, dw, B, cin, cout, N, dtype, st);
   };
   if (dtype == PSA_F32) return go(float{});
   if (dtype == PSA_BF16) return go(psa::bf16{});

@@ -228,12 +228,14 @@ __device__ __forceinline__ u32x4 load8_funnel(const void* p, int avail) {
 
 // Global -> registers -> LDS for a tile of C channel rows x BT tokens from
 // token j0 (tokens >= N read as zero).  Rows [0, SPLIT) come from src_lo and
-// rows [SPLIT, C) from src_hi, both channel-major with row stride N.
+// rows [SPLIT, C) from src_hi, both channel-major with row stride ld (N, or
+// N rounded up to 8 for inputs staged into padded rows, whose tokens past N
+// hold zeros).
 // All C rows go to the channel-major tile nat[row][nat_pitch(BT)].
 //   bf16, fp16: each thread owns 4-channel x 8-token blocks (four 16-byte loads).
 //   fp32: 16-byte chunks (4 tokens of one row).
-// VECOK: N is a multiple of the 16-byte vector, so every chunk is aligned and
-// wholly inside or wholly past the row end.
+// VECOK: ld is a multiple of the 16-byte vector, so every chunk is aligned;
+// a chunk that crosses N (padded rows only) brings the row's zero padding.
 template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT>
 struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   static_assert(is_16bit<T>(), "16-bit element type");
@@ -250,13 +252,15 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   u32x4 r[PER][4];
 
   // One 16-byte chunk (8 tokens of one row) per (u, i); W bytes per load:
-  // 16 when N is a multiple of 8 (VECOK), else 8 or 4 as the rows' alignment
-  // allows (masked per load; a load at token j + k*W/2 < N holds only tokens
-  // below N, as N is a multiple of W/2); for odd N (W = 0) load8_funnel.
+  // 16 when ld is a multiple of 8 (VECOK), else (ld = N) 8 or 4 as the rows'
+  // alignment allows (masked per load; a load at token j + k*W/2 < N holds
+  // only tokens below N, as N is a multiple of W/2); for odd N (W = 0)
+  // load8_funnel.
   // (Measured at N = 6398/6399, dk = dv = 64: 4-byte loads beat the funnel's
   // extra VALU work where they apply; 2-byte loads lose to it.)
   template <int W>
-  __device__ __forceinline__ void load_w(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0, int tid) {
+  __device__ __forceinline__ void load_w(const T* __restrict__ lo, const T* __restrict__ hi, int ld, int N, int j0,
+                                         int tid) {
     constexpr int TPL = W / 2;  // tokens per load
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -264,12 +268,12 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
       const int tc = blk_tc(q), cg = blk_cg(q);
       const int j = j0 + 8 * tc;
       const bool live = NB % NT == 0 || q < NB;
-      const T* base = 4 * cg < SPLIT ? lo + (size_t)(4 * cg) * N : hi + (size_t)(4 * cg - SPLIT) * N;
+      const T* base = 4 * cg < SPLIT ? lo + (size_t)(4 * cg) * ld : hi + (size_t)(4 * cg - SPLIT) * ld;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         r[u][i] = u32x4{0u, 0u, 0u, 0u};
         if (!live) continue;
-        const T* p = base + (size_t)i * N + j;
+        const T* p = base + (size_t)i * ld + j;
         if constexpr (W == 16) {
           if (j < N) r[u][i] = *(const u32x4*)p;
         } else if constexpr (W == 8) {
@@ -289,17 +293,21 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
       }
     }
   }
-  __device__ __forceinline__ void load(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0,
+  __device__ __forceinline__ void load(const T* __restrict__ lo, const T* __restrict__ hi, int ld, int N, int j0,
                                        int tid) {
     if constexpr (VECOK) {
-      load_w<16>(lo, hi, N, j0, tid);
-    } else if ((N & 3) == 0) {  // one uniform branch per call, straight-line loads inside
-      load_w<8>(lo, hi, N, j0, tid);
-    } else if ((N & 1) == 0) {
-      load_w<4>(lo, hi, N, j0, tid);
+      load_w<16>(lo, hi, ld, N, j0, tid);
+    } else if ((ld & 3) == 0) {  // one uniform branch per call, straight-line loads inside
+      load_w<8>(lo, hi, ld, N, j0, tid);
+    } else if ((ld & 1) == 0) {
+      load_w<4>(lo, hi, ld, N, j0, tid);
     } else {
-      load_w<0>(lo, hi, N, j0, tid);
+      load_w<0>(lo, hi, ld, N, j0, tid);
     }
+  }
+  __device__ __forceinline__ void load(const T* __restrict__ lo, const T* __restrict__ hi, int N, int j0,
+                                       int tid) {
+    load(lo, hi, N, N, j0, tid);
   }
   __device__ __forceinline__ void store(T* nat, int tid) const {
 #pragma unroll
@@ -321,15 +329,15 @@ struct Stager<float, C, BT, NT, VECOK, SPLIT> {
   static_assert(BT % 4 == 0, "tile shape");
   f32x4 r[PER];
 
-  __device__ __forceinline__ void load(const float* __restrict__ lo, const float* __restrict__ hi, int N, int j0,
-                                       int tid) {
+  __device__ __forceinline__ void load(const float* __restrict__ lo, const float* __restrict__ hi, int ld, int N,
+                                       int j0, int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
       r[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (CHUNKS % NT != 0 && q >= CHUNKS) continue;
       const int row = q / CPR, j = j0 + (q - row * CPR) * 4;
-      const float* p = (row < SPLIT ? lo + (size_t)row * N : hi + (size_t)(row - SPLIT) * N) + j;
+      const float* p = (row < SPLIT ? lo + (size_t)row * ld : hi + (size_t)(row - SPLIT) * ld) + j;
       if constexpr (VECOK) {
         if (j < N) r[u] = *(const f32x4*)p;
       } else {
@@ -337,6 +345,10 @@ struct Stager<float, C, BT, NT, VECOK, SPLIT> {
         for (int e = 0; e < 4; ++e) r[u][e] = (j + e < N) ? p[e] : 0.f;
       }
     }
+  }
+  __device__ __forceinline__ void load(const float* __restrict__ lo, const float* __restrict__ hi, int N, int j0,
+                                       int tid) {
+    load(lo, hi, N, N, j0, tid);
   }
   __device__ __forceinline__ void store(float* nat, int tid) const {
 #pragma unroll

@@ -28,6 +28,8 @@ constexpr int kConvTile = 128;  // output rows and columns per workgroup
 
 // ------------------------------------------------------------------- dx
 // Workgroup: batch b, ci tile [ci0, ci0 + 128), token tile [n0, n0 + 128).
+// dy rows are ld >= N tokens apart (columns N .. ld - 1 zero, or ld = N);
+// dx rows are N tokens long.
 // co is consumed in chunks of KCH (64, fp32: 32) through a double-buffered
 // pair of channel-major tiles holding w [KCH co][128 ci] and dy [KCH co][128 n].
 //
@@ -49,7 +51,7 @@ struct DxParts {
 template <typename T, bool VECOK>
 __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ w, const T* __restrict__ dy,
                                                           const DxParts<T> parts, int cin, int cout, int N,
-                                                          int n_ntiles, int n_citiles, int n_blocks) {
+                                                          int ld, int n_ntiles, int n_citiles, int n_blocks) {
   constexpr int KCH = is_16bit<T>() ? 64 : 32, BT = kConvTile, NT = 256;  // fp32 tiles are twice as wide
   constexpr int KC = KCH / 32;
   // rows = co (channels of the chunk), tokens = ci (w) or n (dy)
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
   const int b = blk / per_b, r = blk - b * per_b;
   const int nt = r / n_citiles;
   const int ci0 = (r - nt * n_citiles) * BT, n0 = nt * BT;
-  const T* dyb = dy + (size_t)b * cout * N;
+  const T* dyb = dy + (size_t)b * cout * ld;
   const int wr = (wv >> 1) * 64, wc = (wv & 1) * 64;  // this wave's rows (ci) and columns (n)
 
   f32x4 acc[4][4];
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
     sy.store(y, tid);
   };
   sw.load(w, w, cin, ci0, tid);
-  sy.load(dyb, dyb, N, n0, tid);
+  sy.load(dyb, dyb, ld, n0, tid);
   stage(0);
   __syncthreads();
 
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void psa_conv_dx_kernel(const T* __restrict__ 
     const T* y = a + BUF;
     if (k + 1 < nch) {
       sw.load(w + (size_t)(k + 1) * KCH * cin, w + (size_t)(k + 1) * KCH * cin, cin, ci0, tid);
-      sy.load(dyb + (size_t)(k + 1) * KCH * N, dyb + (size_t)(k + 1) * KCH * N, N, n0, tid);
+      sy.load(dyb + (size_t)(k + 1) * KCH * ld, dyb + (size_t)(k + 1) * KCH * ld, ld, n0, tid);
     }
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {

@@ -4,110 +4,21 @@
 // operands are read with transpose reads (w is [co][ci] and dy [co][n], the
 // contraction index the slow one in both).
 //
-// psa_conv_dx_pipe_kernel (N a multiple of 8): 256 x 256 or 128 x 256 tiles,
+// psa_conv_dx_pipe_kernel (dy rows of ld tokens, a multiple of 8, of which
+// the first N count; dx rows of N): 256 x 256 or 128 x 256 tiles,
 // 8 waves, operands brought into LDS by direct global-to-LDS loads three
-// stages ahead.  psa_conv_dx_wide_kernel (other N): 128 x 128 outputs per
-// wave, 4 waves, operands staged through registers into a double-buffered
-// LDS pair.  This file is built without the
-// option that holds MFMA accumulators in ordinary VGPRs (the attention
-// kernels, which rescale and read theirs with VALU instructions, need it):
-// the wide kernel's 256 accumulators per wave live in AGPRs.  Each epilogue
-// writes a dx row into its part of a channel concatenation (see DxParts), as
-// psa_conv_dx_kernel does.
+// stages ahead.  Rows of other lengths reach it through zero-padded copies
+// of dy (the caller's staging).  This file is built without the option that
+// holds MFMA accumulators in ordinary VGPRs (the attention kernels, which
+// rescale and read theirs with VALU instructions, need it), so the
+// accumulators live in AGPRs.  The epilogue writes each dx row into its part
+// of a channel concatenation (see DxParts), as psa_conv_dx_kernel does.
 #include <hip/hip_runtime.h>
 
 #include "psa_conv_wide.h"
 #include "psa_conv_kernels.h"
 
 namespace psa {
-
-// For rows of N not a multiple of 8 (dy staged by load widths the rows'
-// alignment allows).  Workgroup: batch b, WM x WN waves (WM * WN = 4) over a
-// (128 WM) ci x (128 WN) n tile; co in stages of 32 through a double-buffered
-// pair of channel-major tiles w[32 co][128 WM ci] and dy[32 co][128 WN n].
-template <typename T, int WM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void psa_conv_dx_wide_kernel(const T* __restrict__ w, const T* __restrict__ dy, const DxParts<T> parts, int cin,
-                             int cout, int N, int n_ntiles, int n_mtiles, int n_blocks) {
-  constexpr int WN = 4 / WM, BM = 128 * WM, BN = 128 * WN, BK = 32, NT = 256;
-  static_assert(WM * WN == 4, "four waves");
-  using SA = Stager<T, BK, BM, NT, true, BK>;   // w rows co, tokens ci (row stride cin)
-  using SB = Stager<T, BK, BN, NT, false, BK>;  // dy rows co, tokens n (row stride N)
-  constexpr int AE = SA::NAT_ELEMS, BE = SB::NAT_ELEMS;
-  __shared__ __attribute__((aligned(16))) T smem[2 * (AE + BE)];
-
-  const int tid = thread_id(), wv = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
-  // ci tiles innermost: the workgroups that read one dy tile run together on one XCD
-  const int blk = xcd_remap(block_id(), n_blocks);
-  const int per_b = n_ntiles * n_mtiles;
-  const int b = blk / per_b, r = blk - b * per_b;
-  const int nt = r / n_mtiles;
-  const int m0 = (r - nt * n_mtiles) * BM, n0 = nt * BN;
-  const T* dyb = dy + (size_t)b * cout * N;
-  const int wr = (wv % WM) * 128, wc = (wv / WM) * 128;  // this wave's rows (ci) and columns (n)
-
-  f32x4 acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  SA sa;
-  SB sb;
-  sa.load(w, w, cin, m0, tid);
-  sb.load(dyb, dyb, N, n0, tid);
-  sa.store(smem, tid);
-  sb.store(smem + AE, tid);
-  __syncthreads();
-
-  const int nk = cout / BK;
-  for (int k = 0; k < nk; ++k) {
-    const T* at = smem + (k & 1) * (AE + BE);
-    const T* bt = at + AE;
-    if (k + 1 < nk) {
-      sa.load(w + (size_t)(k + 1) * BK * cin, w, cin, m0, tid);
-      sb.load(dyb + (size_t)(k + 1) * BK * N, dyb, N, n0, tid);
-    }
-    Frag<T> fa[8], fb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) frag_tok<BK, false>(fa[i], at, SA::LDN, wr + 16 * i, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) frag_tok<BK, false>(fb[j], bt, SB::LDN, wc + 16 * j, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mma(acc[i][j], fa[i], fb[j]);
-    if (k + 1 < nk) {
-      T* nx = smem + ((k + 1) & 1) * (AE + BE);
-      sa.store(nx, tid);
-      sb.store(nx + AE, tid);
-    }
-    __syncthreads();
-  }
-
-  // acc[i][j]: row ci = m0 + wr + 16i + 4g + rr, column n = n0 + wc + 16j + t.
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int ci = m0 + wr + 16 * i + 4 * g + rr;
-      T* base = parts.p[0];
-      int first = 0, ch = parts.ch[0];
-#pragma unroll
-      for (int q = 1; q < kCatMaxParts; ++q)
-        if (q < parts.n && ci >= parts.begin[q]) {
-          base = parts.p[q];
-          first = parts.begin[q];
-          ch = parts.ch[q];
-        }
-      T* row = base + ((size_t)b * ch + (ci - first)) * N;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = n0 + wc + 16 * j + t;
-        if (n < N) row[n] = from_f32<T>(acc[i][j][rr]);
-      }
-    }
-}
 
 // 16-byte direct global-to-LDS load: lane l's 16 bytes from g land at
 // lds + 16 l (lds wave-uniform, passed in M0).  Written as inline asm so that
@@ -188,7 +99,7 @@ __device__ __forceinline__ void frag_lds(Frag<T>& f, const unsigned char* p, int
 template <typename T, int BM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, const DxParts<T> parts, int cin,
-                             int cout, int N, int n_ntiles, int n_mtiles, int n_blocks) {
+                             int cout, int N, int ld, int n_ntiles, int n_mtiles, int n_blocks) {
   static_assert(BM == 256 || BM == 128, "ci tile");
   constexpr int NW = 8, BN = 256, BK = 32, JN = 4;  // JN: 16-token fragments per wave
   constexpr int IA = BM / 32;                       // 16-channel fragments per wave
@@ -205,7 +116,7 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
   const int b = blk / per_b, r = blk - b * per_b;
   const int nt = r / n_mtiles;
   const int m0 = (r - nt * n_mtiles) * BM, n0 = nt * BN;
-  const T* dyb = dy + (size_t)b * cout * N;
+  const T* dyb = dy + (size_t)b * cout * ld;
   const int wr = (wv & 1) * (BM / 2), wc = (wv >> 1) * 16 * JN;  // this wave's rows (ci) and columns (n)
 
   // This lane's source of each direct load of a stage (element offsets):
@@ -220,12 +131,12 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
   for (int i = 0; i < BI; ++i) {
     const int slot = wv * BI + i, p = lane / (64 / TB::Q), x = lane % (64 / TB::Q);
     const int n = n0 + 8 * x;
-    b_src[i] = TB::channel(slot, p) * N + (n < N ? n : n0);  // chunks past N read a valid one; unstored columns
+    b_src[i] = TB::channel(slot, p) * ld + (n < N ? n : n0);  // chunks past N read a valid one; unstored columns
   }
   auto issue = [&](int kk, int slot) {
     const unsigned char* sb = smem + slot * SB;
     const T* wa = w + (size_t)kk * BK * cin;
-    const T* db = dyb + (size_t)kk * BK * N;
+    const T* db = dyb + (size_t)kk * BK * ld;
 #pragma unroll
     for (int i = 0; i < AI; ++i) lds_dma16(wa + a_src[i], sb + (wv * AI + i) * TA::IB);
 #pragma unroll
@@ -296,66 +207,52 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
 
 namespace {
 
-// Large-tile kernels need this many workgroups (one per CU) to pay off.
+// The pipeline needs this many workgroups (one per CU) to pay off.
 // Measured (bf16, us, against the 64 x 64-wave kernel): B 4, cin 512, cout
-// 1536, N 6400: 256 x 256 pipeline (200 tiles) 49-52, 128 x 256 (400) 54,
-// small tiles 72-74; B 8, cin 512, cout 1024, N 1600: 256 x 256 (112 tiles)
-// 35, 128 x 256 (224) 24, small tiles 30; register-staged 256 x 256 at
-// N = 6399 (200 tiles) 181-203 vs 277.
+// 1536, N 6400: 256 x 256 (200 tiles) 49-52, 128 x 256 (400) 54, small
+// tiles 72-74; B 8, cin 512, cout 1024, N 1600: 256 x 256 (112 tiles) 35,
+// 128 x 256 (224) 24, small tiles 30.
 constexpr long long kPipe256MinBlocks = 192;
 constexpr long long kPipe128MinBlocks = 128;
-constexpr long long kStagedMinBlocks = 128;
 
 long long tiles(int B, int cin, int N, int bm, int bn) {
   return (long long)B * (cin / bm) * ((N + bn - 1) / bn);
 }
 
 template <typename T, int BM>
-void pipe(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N, hipStream_t st) {
+void pipe(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N, int ld,
+          hipStream_t st) {
   const int n_mtiles = cin / BM, n_ntiles = (N + 255) / 256, blocks = B * n_mtiles * n_ntiles;
   hipLaunchKernelGGL((psa_conv_dx_pipe_kernel<T, BM>), dim3(blocks), dim3(512), 0, st, (const T*)w, (const T*)dy, dx,
-                     cin, cout, N, n_ntiles, n_mtiles, blocks);
-}
-
-template <typename T, int WM>
-void staged(const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N, hipStream_t st) {
-  constexpr int BM = 128 * WM, BN = 128 * (4 / WM);
-  const int n_mtiles = cin / BM, n_ntiles = (N + BN - 1) / BN, blocks = B * n_mtiles * n_ntiles;
-  hipLaunchKernelGGL((psa_conv_dx_wide_kernel<T, WM>), dim3(blocks), dim3(256), 0, st, (const T*)w, (const T*)dy,
-                     dx, cin, cout, N, n_ntiles, n_mtiles, blocks);
+                     cin, cout, N, ld, n_ntiles, n_mtiles, blocks);
 }
 
 template <typename T>
 void launch(DxLarge kind, const void* w, const void* dy, const DxParts<T>& dx, int B, int cin, int cout, int N,
-            hipStream_t st) {
+            int ld, hipStream_t st) {
   switch (kind) {
-    case DxLarge::pipe256: pipe<T, 256>(w, dy, dx, B, cin, cout, N, st); break;
-    case DxLarge::pipe128: pipe<T, 128>(w, dy, dx, B, cin, cout, N, st); break;
-    case DxLarge::staged256: staged<T, 2>(w, dy, dx, B, cin, cout, N, st); break;
-    case DxLarge::staged128: staged<T, 1>(w, dy, dx, B, cin, cout, N, st); break;
+    case DxLarge::pipe256: pipe<T, 256>(w, dy, dx, B, cin, cout, N, ld, st); break;
+    case DxLarge::pipe128: pipe<T, 128>(w, dy, dx, B, cin, cout, N, ld, st); break;
     case DxLarge::none: break;
   }
 }
 
 }  // namespace
 
-DxLarge conv_dx_large_kind(int B, int cin, int N) {
-  if (N % 8 == 0) {  // 16-byte rows of a 16-bit type
-    if (cin % 256 == 0 && tiles(B, cin, N, 256, 256) >= kPipe256MinBlocks) return DxLarge::pipe256;
-    if (tiles(B, cin, N, 128, 256) >= kPipe128MinBlocks) return DxLarge::pipe128;
-    return DxLarge::none;
-  }
-  if (cin % 256 == 0) return tiles(B, cin, N, 256, 256) >= kStagedMinBlocks ? DxLarge::staged256 : DxLarge::none;
-  return tiles(B, cin, N, 128, 512) >= kStagedMinBlocks ? DxLarge::staged128 : DxLarge::none;
+DxLarge conv_dx_large_kind(int B, int cin, int N, int ld) {
+  if (ld % 8 != 0) return DxLarge::none;  // 16-byte rows of a 16-bit type only
+  if (cin % 256 == 0 && tiles(B, cin, N, 256, 256) >= kPipe256MinBlocks) return DxLarge::pipe256;
+  if (tiles(B, cin, N, 128, 256) >= kPipe128MinBlocks) return DxLarge::pipe128;
+  return DxLarge::none;
 }
 
 void conv_dx_large_launch(DxLarge kind, const void* w, const void* dy, const DxParts<bf16>& dx, int B, int cin,
-                          int cout, int N, hipStream_t st) {
-  launch<bf16>(kind, w, dy, dx, B, cin, cout, N, st);
+                          int cout, int N, int ld, hipStream_t st) {
+  launch<bf16>(kind, w, dy, dx, B, cin, cout, N, ld, st);
 }
 void conv_dx_large_launch(DxLarge kind, const void* w, const void* dy, const DxParts<f16>& dx, int B, int cin,
-                          int cout, int N, hipStream_t st) {
-  launch<f16>(kind, w, dy, dx, B, cin, cout, N, st);
+                          int cout, int N, int ld, hipStream_t st) {
+  launch<f16>(kind, w, dy, dx, B, cin, cout, N, ld, st);
 }
 
 }  // namespace psa

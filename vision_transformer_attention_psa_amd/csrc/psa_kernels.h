@@ -52,8 +52,11 @@ template <int D> struct Chunks {
 // of V; a call over a slice of V has cs = 2dk + dv_total and DV = its own
 // width).  accum != 0: the backward adds its dQ and dK to what d_packed
 // holds instead of overwriting them (dV rows are always overwritten).
+// ld: row stride of the inputs (qkv, and o and dO in the backward): N, or N
+// rounded up to 8 when they were staged into zero-padded rows; outputs
+// (o, lse, d_packed, statistics) always have rows of N.
 struct PackView {
-  int cs, voff, accum;
+  int cs, voff, accum, ld;
 };
 
 // =================================================================== forward
@@ -77,15 +80,16 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int blk = xcd_remap(block_id(), n_blocks);
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
-  const T* Qg = qkv + (size_t)bh * pv.cs * N;
-  const T* KVg = Qg + (size_t)DK * N;
-  const T* Vg = Qg + (size_t)pv.voff * N;
+  const int ld = pv.ld;
+  const T* Qg = qkv + (size_t)bh * pv.cs * ld;
+  const T* KVg = Qg + (size_t)DK * ld;
+  const T* Vg = Qg + (size_t)pv.voff * ld;
 
   // Stationary queries: B operands of S^T = K Q^T (lane = query column).
   Frag<T> qf[QB][KC];
   {
     SQ sq;
-    sq.load(Qg, Qg, N, i0, tid);
+    sq.load(Qg, Qg, ld, N, i0, tid);
     sq.store(smem, tid);
     __syncthreads();
 #pragma unroll
@@ -98,7 +102,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   }
 
   SKV st;
-  st.load(KVg, Vg, N, 0, tid);
+  st.load(KVg, Vg, ld, N, 0, tid);
   st.store(smem, tid);
   __syncthreads();
 
@@ -121,7 +125,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   for (int kt = 0; kt < nkt; ++kt) {
     T* nat = smem + (kt & 1) * BUF;
     const T* Vt = nat + DK * SKV::LDN;
-    if (kt + 1 < nkt) st.load(KVg, Vg, N, (kt + 1) * BN, tid);
+    if (kt + 1 < nkt) st.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
     const int j0 = kt * BN;
 
 #pragma unroll
@@ -227,24 +231,39 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
 // accumulator input as they are; four consecutive queries are one 16-byte
 // LDS read.
 //
-// VEC = false: one thread per query, walking the dv channels.
-// VEC = true (N a multiple of the 16-byte vector): lane (tg, cg) of a wave
+// VEC = true (ld a multiple of the 16-byte vector): lane (tg, cg) of a wave
 // owns the 16-byte token group tg (8 bf16/fp16 or 4 fp32 tokens) and the
 // channel group cg (dv / 8 channels), so that each lane issues all its loads
-// at once; the 8 channel groups' partial sums are then added across lanes.
+// at once; the 8 channel groups' partial sums are then added across lanes,
+// as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)).
+// VEC = false: one thread per query, walking the dv channels with the same
+// 8 partial sums added in the same order, so both variants give the same
+// bits (padded and unpadded rows of one input give one result).
+// o and dO rows have stride ld (>= N; tokens past N are zero padding and
+// write nothing); lse and the two planes have rows of N.
 template <typename T, int DV, bool VEC>
 __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dO,
                                                           const float* __restrict__ lse, float* __restrict__ stats,
-                                                          int N, int total) {
+                                                          int N, int ld, int total) {
   if constexpr (!VEC) {
     const int idx = block_id() * 256 + thread_id();
     if (idx >= total) return;
     const int bh = idx / N, i = idx - bh * N;
-    const T* op = o + (size_t)bh * DV * N + i;
-    const T* gp = dO + (size_t)bh * DV * N + i;
-    float d = 0.f;
-#pragma unroll 16
-    for (int ch = 0; ch < DV; ++ch) d = __builtin_fmaf(to_f32(op[(size_t)ch * N]), to_f32(gp[(size_t)ch * N]), d);
+    const T* op = o + (size_t)bh * DV * ld + i;
+    const T* gp = dO + (size_t)bh * DV * ld + i;
+    constexpr int NCG = 8, CPT = DV / NCG;
+    static_assert(DV % NCG == 0, "channel groups");
+    float p[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      p[cg] = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const size_t off = (size_t)(cg * CPT + c) * ld;
+        p[cg] = __builtin_fmaf(to_f32(op[off]), to_f32(gp[off]), p[cg]);
+      }
+    }
+    const float d = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     stats[idx] = -lse[idx] * kLog2e;
     stats[(size_t)total + idx] = -d;
   } else {
@@ -253,19 +272,19 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
     typedef T V __attribute__((ext_vector_type(TV)));
     const int tid = thread_id(), lane = tid & 63, tg = lane & 7, cg = lane >> 3;
     const int grp = (block_id() * 4 + (tid >> 6)) * 8 + tg;  // 16-byte token group
-    const int gpr = N / TV;                                   // token groups per slice
-    const bool live = grp < total / TV;
+    const int gpr = ld / TV;                                  // token groups per slice
+    const int bh = grp / gpr, i0 = (grp - bh * gpr) * TV;
+    const bool live = bh < total / N;
     float d[TV];
 #pragma unroll
     for (int e = 0; e < TV; ++e) d[e] = 0.f;
     if (live) {
-      const int bh = grp / gpr, i0 = (grp - bh * gpr) * TV;
-      const size_t base = ((size_t)bh * DV + cg * CPT) * N + i0;
+      const size_t base = ((size_t)bh * DV + cg * CPT) * ld + i0;
       V ov[CPT], gv[CPT];
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        ov[c] = *(const V*)(o + base + (size_t)c * N);
-        gv[c] = *(const V*)(dO + base + (size_t)c * N);
+        ov[c] = *(const V*)(o + base + (size_t)c * ld);
+        gv[c] = *(const V*)(dO + base + (size_t)c * ld);
       }
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
@@ -280,14 +299,32 @@ __global__ __launch_bounds__(256) void psa_bwd_pre_kernel(const T* __restrict__ 
       d[e] += __shfl_xor(d[e], 32);
     }
     if (live && cg == 0) {
-      const size_t q0 = (size_t)grp * TV;
+      const size_t q0 = (size_t)bh * N + i0;
 #pragma unroll
-      for (int e = 0; e < TV; ++e) {
-        stats[q0 + e] = -lse[q0 + e] * kLog2e;
-        stats[(size_t)total + q0 + e] = -d[e];
-      }
+      for (int e = 0; e < TV; ++e)
+        if (i0 + e < N) {
+          stats[q0 + e] = -lse[q0 + e] * kLog2e;
+          stats[(size_t)total + q0 + e] = -d[e];
+        }
     }
   }
+}
+
+// Copies rows of n elements (16-bit) into rows of ld (a multiple of 8) with
+// zeros past n: the inputs of a call whose N is not a multiple of 8, so that
+// the kernels stage them with aligned 16-byte loads.  One 16-byte output
+// chunk per thread; load8_funnel reads the source rows.
+template <typename T>
+__global__ __launch_bounds__(256) void psa_pad_rows_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                           long long rows, int n, int ld) {
+  static_assert(is_16bit<T>(), "16-bit element type");
+  const long long q = (long long)block_id() * 256 + thread_id();
+  const int cpr = ld / 8;
+  if (q >= rows * cpr) return;
+  const long long r = q / cpr;
+  const int j = (int)(q - r * cpr) * 8;
+  const u32x4 v = j < n ? load8_funnel(src + r * n + j, n - j) : u32x4{0u, 0u, 0u, 0u};
+  *(u32x4*)(dst + r * ld + j) = v;
 }
 
 // ============================================================ backward dK/dV
@@ -328,10 +365,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int bh = blk / n_ktiles, j0 = (blk - bh * n_ktiles) * BNK;
   const size_t C = pv.cs;
-  const T* Qg = qkv + (size_t)bh * C * N;
-  const T* KVg = Qg + (size_t)DK * N;
-  const T* Vg = Qg + (size_t)pv.voff * N;
-  const T* dOg = dO + (size_t)bh * DV * N;
+  const int ld = pv.ld;
+  const T* Qg = qkv + (size_t)bh * C * ld;
+  const T* KVg = Qg + (size_t)DK * ld;
+  const T* Vg = Qg + (size_t)pv.voff * ld;
+  const T* dOg = dO + (size_t)bh * DV * ld;
   const float* nlq = nlg + (size_t)bh * N;
   const float* ndq = ndg + (size_t)bh * N;
 
@@ -339,7 +377,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   Frag<T> kf[KB][KC], vf[KB][CC];
   {
     SKV sk;
-    sk.load(KVg, Vg, N, j0, tid);
+    sk.load(KVg, Vg, ld, N, j0, tid);
     sk.store(smem, tid);
     __syncthreads();
 #pragma unroll
@@ -367,7 +405,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   }
 
   SQG sg;
-  sg.load(Qg, dOg, N, 0, tid);
+  sg.load(Qg, dOg, ld, N, 0, tid);
   sg.store(smem, tid);
   for (int q = tid; q < BMQ; q += NT) {  // padding rows: P = 0
     snl[q] = q < N ? nlq[q] : kNegInf;
@@ -386,9 +424,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   float pnl = kNegInf, pnd = 0.f;
   auto load_tile = [&](int qt, int lt) {  // rows and statistics of query tile qt (lt = thread index)
     if constexpr (DEEP)
-      sh.load(Qg, dOg, N, qt * BMQ, lt);
+      sh.load(Qg, dOg, ld, N, qt * BMQ, lt);
     else
-      sg.load(Qg, dOg, N, qt * BMQ, lt);
+      sg.load(Qg, dOg, ld, N, qt * BMQ, lt);
     const int q = qt * BMQ + lt;
     pnl = kNegInf, pnd = 0.f;
     if (lt < BMQ && q < N) {  // padding queries: P = 0
@@ -551,10 +589,11 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int bh = blk / n_qtiles, i0 = (blk - bh * n_qtiles) * BM;
   const size_t C = pv.cs;
-  const T* Qg = qkv + (size_t)bh * C * N;
-  const T* KVg = Qg + (size_t)DK * N;
-  const T* Vg = Qg + (size_t)pv.voff * N;
-  const T* dOg = dO + (size_t)bh * DV * N;
+  const int ld = pv.ld;
+  const T* Qg = qkv + (size_t)bh * C * ld;
+  const T* KVg = Qg + (size_t)DK * ld;
+  const T* Vg = Qg + (size_t)pv.voff * ld;
+  const T* dOg = dO + (size_t)bh * DV * ld;
 
   // Stationary queries: B operands of S^T = K Q^T and dP^T = V dO^T.  Their
   // LSE (log2 units, negated) and -D are per lane (lane column = query).
@@ -562,7 +601,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   float nl[QB], nd[QB];
   {
     SQG sq;
-    sq.load(Qg, dOg, N, i0, tid);
+    sq.load(Qg, dOg, ld, N, i0, tid);
     sq.store(smem, tid);
     __syncthreads();
 #pragma unroll
@@ -590,14 +629,14 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
     for (int db = 0; db < DK / 16; ++db) dqacc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   SKV sk;
-  sk.load(KVg, Vg, N, 0, tid);
+  sk.load(KVg, Vg, ld, N, 0, tid);
   sk.store(smem, tid);
   __syncthreads();
 
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
     const T* nat = smem + (kt & 1) * BUF;  // K then V channels, channel-major
-    if (kt + 1 < nkt) sk.load(KVg, Vg, N, (kt + 1) * BN, tid);
+    if (kt + 1 < nkt) sk.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
 
 #pragma unroll
     for (int c2 = 0; c2 < BN / 32; ++c2) {

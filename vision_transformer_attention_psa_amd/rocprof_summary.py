@@ -25,7 +25,7 @@ from collections import defaultdict
 
 PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
              ("psa_bwd_fused_kernel", "bwd_main"), ("psa_conv_dx_kernel", "conv_dx"),
-             ("psa_conv_dx_pipe_kernel", "conv_dx_pipe"), ("psa_conv_dx_wide_kernel", "conv_dx_wide"),
+             ("psa_conv_dx_pipe_kernel", "conv_dx_pipe"), ("psa_pad_rows_kernel", "pad_rows"),
              ("psa_conv_dw_reduce_kernel", "conv_dw_reduce"), ("psa_conv_dw_kernel", "conv_dw"),
              ("psa_rows_copy_kernel", "rows_copy"))
 
