@@ -287,7 +287,9 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, ps
   const float c = scale * psa::kLog2e;
   const dim3 g((unsigned)grid), b(C::FWD_NW * 64);
   TimedLaunch tl(K_FWD, st);
-  if (vec_ok<T>(pv.ld))
+  // The aligned instance (16-byte loads; for 16-bit types direct loads into
+  // LDS) addresses a slice with 32-bit element offsets.
+  if (vec_ok<T>(pv.ld) && (long long)pv.cs * pv.ld < INT32_MAX)
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true, C::FWD_OCC>), g, b, 0, st,
                        (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   else

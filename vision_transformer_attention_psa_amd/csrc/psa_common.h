@@ -361,6 +361,76 @@ struct Stager<float, C, BT, NT, VECOK, SPLIT> {
   }
 };
 
+// 16-byte direct global-to-LDS load: lane l's 16 bytes from g land at
+// lds + 16 l (lds wave-uniform, passed in M0).  Written as inline asm so that
+// the compiler does not treat the loads still in flight as pending writes to
+// every later LDS read (it would wait for all of them before the first
+// one); the kernel orders them itself with barrier_vmcnt.  The instruction
+// has no register result, so nothing the compiler allocates is written late.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(a) : "memory");
+}
+
+// Workgroup barrier once this wave's LDS reads and all but its last NV
+// vector-memory operations have completed (lgkmcnt 0, vmcnt NV; gfx9
+// s_waitcnt encoding, expcnt left at its maximum).  Unlike __syncthreads it
+// does not wait for every load in flight; the signal fences keep the
+// compiler from moving memory accesses across it.
+template <int NV>
+__device__ __forceinline__ void barrier_vmcnt() {
+  static_assert(NV >= 0 && NV < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((NV & 15) | (7 << 4) | ((NV >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Direct global-to-LDS staging of a C-row x BT-token 16-bit tile (channel
+// rows, row stride ld a multiple of 8) into the layout Stager::store writes
+// (row pitch nat_pitch(BT) = BT + 8 elements), with no register round trip.
+// LDS slot s (16 bytes) of a stage holds token chunk s % (TC + 1) of row
+// s / (TC + 1); chunk TC is the row's pad (filled from a valid address and
+// never read).  Each of the NW waves owns L 1 KB loads of 64 slots and
+// issues those that hold part of the tile (wv is wave-uniform).  Rows [0, SPLIT) start at element
+// lo_off of the base pointer, rows [SPLIT, C) at hi_off, both in rows of ld.
+// Chunks past the row's end are loaded from its last full chunk (ld - 8):
+// their values are finite data of the same row, and the caller gives those
+// tokens zero weight.
+template <typename T, int C, int BT, int NW, int SPLIT>
+struct DmaStage {
+  static_assert(is_16bit<T>(), "16-bit element type");
+  static constexpr int TC = BT / 8, SLOTS = C * (TC + 1), LOADS = (SLOTS + 63) / 64;
+  static constexpr int L = (LOADS + NW - 1) / NW;  // loads per wave
+  static constexpr int BYTES = NW * L * 1024;      // LDS bytes of one stage
+  static constexpr int ELEMS = BYTES / (int)sizeof(T);
+  static_assert(BYTES >= C * nat_pitch<T>(BT) * (int)sizeof(T), "stage holds the tile");
+  int off[L];  // this lane's element offset from the base pointer at token 0
+  int tok[L];  // its chunk's first token within the tile
+
+  __device__ __forceinline__ void init(int wv, int lane, int lo_off, int hi_off, int ld) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int s = 64 * (wv * L + i) + lane;
+      int r = s / (TC + 1), c = s - r * (TC + 1);
+      if (r >= C) r = C - 1, c = 0;  // past the tile
+      if (c == TC) c = TC - 1;       // the row's pad
+      off[i] = (r < SPLIT ? lo_off + r * ld : hi_off + (r - SPLIT) * ld);
+      tok[i] = 8 * c;
+    }
+  }
+  // Loads of the tile at token j0 into the stage at `lds`.
+  __device__ __forceinline__ void issue(const T* base, int j0, int ld, const void* lds, int wv) const {
+    const unsigned char* st = (const unsigned char*)lds + wv * L * 1024;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (LOADS % NW != 0 && wv * L + i >= LOADS) break;
+      const int j = min(j0 + tok[i], ld - 8);
+      lds_dma16(base + off[i] + j, st + i * 1024);
+    }
+  }
+};
+
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Remap so
 // that consecutive logical ids (tiles of one (batch, head) slice, which share
 // K/V or Q/dO) run on the same XCD and share its L2.  Bijective for any n.

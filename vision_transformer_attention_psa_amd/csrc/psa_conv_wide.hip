@@ -20,31 +20,6 @@
 
 namespace psa {
 
-// 16-byte direct global-to-LDS load: lane l's 16 bytes from g land at
-// lds + 16 l (lds wave-uniform, passed in M0).  Written as inline asm so that
-// the compiler does not treat the loads still in flight as pending writes to
-// every later LDS read (it would wait for all of them before the first
-// one); the kernel orders them itself with barrier_vmcnt.  The instruction
-// has no register result, so nothing the compiler allocates is written late.
-__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
-  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(a) : "memory");
-}
-
-// Workgroup barrier once this wave's LDS reads and all but its last NV
-// vector-memory operations have completed (lgkmcnt 0, vmcnt NV; gfx9
-// s_waitcnt encoding, expcnt left at its maximum).  Unlike __syncthreads it
-// does not wait for every load in flight; the signal fences keep the
-// compiler from moving memory accesses across it.
-template <int NV>
-__device__ __forceinline__ void barrier_vmcnt() {
-  static_assert(NV >= 0 && NV < 64, "vmcnt range");
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt((NV & 15) | (7 << 4) | ((NV >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // LDS layout of one [32 channel][RE token] 16-bit tile filled by 1 KB direct
 // loads (Q = 1024 / row bytes rows per load).  A transpose read (frag_tr's
 // lane pattern) has each half-wave read 32 bytes from each of 8 rows whose

@@ -69,13 +69,17 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   constexpr int KC = Chunks<DK>::n;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
   // K|V tile, channel-major: K rows read as token rows for S^T, V rows as
-  // channel rows for PV.
+  // channel rows for PV.  16-bit types with 16-byte rows (VECOK) bring it
+  // into LDS by direct loads (DKV), others through registers (SKV); both
+  // write the same layout.
+  constexpr bool DMA = VECOK && is_16bit<T>();
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK>;
+  using DKV = DmaStage<std::conditional_t<DMA, T, bf16>, DK + DV, DMA ? BN : 32, NW, DK>;
   using SQ = Stager<T, DK, BM, NT, VECOK, DK>;
-  constexpr int BUF = SKV::NAT_ELEMS;
+  constexpr int BUF = DMA ? DKV::ELEMS : SKV::NAT_ELEMS;
   constexpr int QE = SQ::NAT_ELEMS;
   constexpr int SMEM = 2 * BUF > QE ? 2 * BUF : QE;
-  __shared__ __attribute__((aligned(16))) T smem[SMEM];
+  __shared__ __attribute__((aligned(1024))) T smem[SMEM];
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
   const int blk = xcd_remap(block_id(), n_blocks);
@@ -102,9 +106,17 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   }
 
   SKV st;
-  st.load(KVg, Vg, ld, N, 0, tid);
-  st.store(smem, tid);
-  __syncthreads();
+  DKV dst;
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  if constexpr (DMA) {
+    dst.init(wv, lane, DK * ld, pv.voff * ld, ld);
+    dst.issue(Qg, 0, ld, smem, wv);
+    barrier_vmcnt<0>();
+  } else {
+    st.load(KVg, Vg, ld, N, 0, tid);
+    st.store(smem, tid);
+    __syncthreads();
+  }
 
   const Frag<T> ones = ones_frag<T>();
   // m: running column maximum (log2 units, scale included); thr: the raw
@@ -125,7 +137,13 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   for (int kt = 0; kt < nkt; ++kt) {
     T* nat = smem + (kt & 1) * BUF;
     const T* Vt = nat + DK * SKV::LDN;
-    if (kt + 1 < nkt) st.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
+    if (kt + 1 < nkt) {
+      // the other stage was last read before the previous iteration's barrier
+      if constexpr (DMA)
+        dst.issue(Qg, (kt + 1) * BN, ld, smem + ((kt + 1) & 1) * BUF, wv);
+      else
+        st.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
+    }
     const int j0 = kt * BN;
 
 #pragma unroll
@@ -200,11 +218,15 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
       }
     }
 
-    if (kt + 1 < nkt) {
-      T* nx = smem + ((kt + 1) & 1) * BUF;
-      st.store(nx, tid);
+    if constexpr (DMA) {
+      barrier_vmcnt<0>();  // this wave's loads of the next tile landed, then everyone's
+    } else {
+      if (kt + 1 < nkt) {
+        T* nx = smem + ((kt + 1) & 1) * BUF;
+        st.store(nx, tid);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // Epilogue: every row of the ones-product holds the column sum l.
