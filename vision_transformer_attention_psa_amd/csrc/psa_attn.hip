@@ -334,7 +334,8 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   {
     TimedLaunch tl(K_MAIN, st);
     const dim3 grid((unsigned)(nkb + nqb)), block(NW * 64);
-    if (vec_ok<T>(pv.ld))
+    // as in the forward: 32-bit element offsets within a slice
+    if (vec_ok<T>(pv.ld) && (long long)pv.cs * pv.ld < INT32_MAX)
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, true, C::DKDV_DEEP>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);

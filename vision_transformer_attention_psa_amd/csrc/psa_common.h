@@ -391,9 +391,10 @@ __device__ __forceinline__ void barrier_vmcnt() {
 // (row pitch nat_pitch(BT) = BT + 8 elements), with no register round trip.
 // LDS slot s (16 bytes) of a stage holds token chunk s % (TC + 1) of row
 // s / (TC + 1); chunk TC is the row's pad (filled from a valid address and
-// never read).  Each of the NW waves owns L 1 KB loads of 64 slots and
-// issues those that hold part of the tile (wv is wave-uniform).  Rows [0, SPLIT) start at element
-// lo_off of the base pointer, rows [SPLIT, C) at hi_off, both in rows of ld.
+// never read).  Each of the NW waves owns L 1 KB loads of 64 slots (wv is
+// wave-uniform) and issues those of them that exist.  Rows [0, SPLIT) start
+// at element lo_off of the base pointer, rows [SPLIT, C) at hi_off, both in
+// rows of ld.
 // Chunks past the row's end are loaded from its last full chunk (ld - 8):
 // their values are finite data of the same row, and the caller gives those
 // tokens zero weight.
@@ -402,7 +403,7 @@ struct DmaStage {
   static_assert(is_16bit<T>(), "16-bit element type");
   static constexpr int TC = BT / 8, SLOTS = C * (TC + 1), LOADS = (SLOTS + 63) / 64;
   static constexpr int L = (LOADS + NW - 1) / NW;  // loads per wave
-  static constexpr int BYTES = NW * L * 1024;      // LDS bytes of one stage
+  static constexpr int BYTES = LOADS * 1024;       // LDS bytes of one stage
   static constexpr int ELEMS = BYTES / (int)sizeof(T);
   static_assert(BYTES >= C * nat_pitch<T>(BT) * (int)sizeof(T), "stage holds the tile");
   int off[L];  // this lane's element offset from the base pointer at token 0

@@ -585,10 +585,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 template <typename T, int DK, int DV, int QB, int NW, int BN>
 struct DqShape {
   static constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
-  // Streamed K|V tile and stationary Q|dO tile, both channel-major.
+  // Streamed K|V tile and stationary Q|dO tile, both channel-major.  16-bit
+  // types stream K|V by direct loads where rows are 16-byte aligned: a
+  // stage is BN / SUB sub-tiles of SUB keys (DKV, one set of per-lane
+  // offsets for all of them), each in the layout the register staging (SKV)
+  // gives a whole tile; a stage has room for either.
+  static constexpr int SUB = BN < 64 ? BN : 64, NSUB = BN / SUB;
   using SKV = Stager<T, DK + DV, BN, NT, true, DK>;
+  using DKV = DmaStage<std::conditional_t<is_16bit<T>(), T, bf16>, DK + DV, SUB, NW, DK>;
   using SQG = Stager<T, DK + DV, BM, NT, true, DK>;
-  static constexpr int BUF = SKV::NAT_ELEMS;
+  static constexpr int DBUF = NSUB * DKV::ELEMS;
+  static constexpr int BUF = is_16bit<T>() && DBUF > SKV::NAT_ELEMS ? DBUF : (int)SKV::NAT_ELEMS;
   static constexpr int QE = SQG::NAT_ELEMS;
   static constexpr int SMEM = (2 * BUF > QE ? 2 * BUF : QE) * (int)sizeof(T);
 };
@@ -602,10 +609,11 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   constexpr int QW = Shape::QW, BM = Shape::BM, NT = Shape::NT;
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
+  constexpr bool DMA = VECOK && is_16bit<T>();
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK>;
+  using DKV = typename Shape::DKV;
   using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK>;
-  constexpr int BUF = SKV::NAT_ELEMS;
-  static_assert(BUF == Shape::BUF, "tile layout");
+  constexpr int BUF = Shape::BUF;
   T* smem = (T*)smem_raw;
 
   const int tid = thread_id(), w = tid >> 6, lane = tid & 63, g = lane >> 4, t = lane & 15;
@@ -651,14 +659,43 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
     for (int db = 0; db < DK / 16; ++db) dqacc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   SKV sk;
-  sk.load(KVg, Vg, ld, N, 0, tid);
-  sk.store(smem, tid);
-  __syncthreads();
+  DKV dkv;
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  constexpr int SUB = Shape::SUB, NSUB = Shape::NSUB;
+  auto issue = [&](int j0, T* stage) {
+    if constexpr (DMA) {
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) dkv.issue(Qg, j0 + u * SUB, ld, stage + u * DKV::ELEMS, wv);
+    }
+  };
+  // Where chunk c2's 32 keys sit: sub-tile c2 / (SUB / 32) of a direct-load
+  // stage, or the register-staged tile.
+  constexpr int LDN = DMA ? nat_pitch<T>(SUB) : SKV::LDN;
+  auto chunk = [&](const T* nat, int c2) -> const T* {
+    return DMA ? nat + (c2 / (SUB / 32)) * DKV::ELEMS : nat;
+  };
+  auto ckey = [&](int c2) { return DMA ? 32 * (c2 % (SUB / 32)) : 32 * c2; };
+  if constexpr (DMA) {
+    dkv.init(wv, lane, DK * ld, pv.voff * ld, ld);
+    issue(0, smem);
+    barrier_vmcnt<0>();
+  } else {
+    sk.load(KVg, Vg, ld, N, 0, tid);
+    sk.store(smem, tid);
+    __syncthreads();
+  }
 
   const int nkt = (N + BN - 1) / BN;
   for (int kt = 0; kt < nkt; ++kt) {
     const T* nat = smem + (kt & 1) * BUF;  // K then V channels, channel-major
-    if (kt + 1 < nkt) sk.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
+    const int j0 = kt * BN;
+    if (kt + 1 < nkt) {
+      // the other stage was last read before the previous iteration's barrier
+      if constexpr (DMA)
+        issue((kt + 1) * BN, smem + ((kt + 1) & 1) * BUF);
+      else
+        sk.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
+    }
 
 #pragma unroll
     for (int c2 = 0; c2 < BN / 32; ++c2) {
@@ -674,20 +711,33 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          frag_tok<DK, true>(a, nat, SKV::LDN, 32 * c2, h, 32 * kc);
+          frag_tok<DK, true>(a, chunk(nat, c2), LDN, ckey(c2), h, 32 * kc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
           Frag<T> a;
-          frag_tok<DV, true>(a, nat + DK * SKV::LDN, SKV::LDN, 32 * c2, h, 32 * cc);
+          frag_tok<DV, true>(a, chunk(nat, c2) + DK * LDN, LDN, ckey(c2), h, 32 * cc);
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }
+        // Keys past N: direct loads leave other tokens' (finite) values in
+        // their K and V rows, so their scores get zero weight here; the
+        // register staging leaves zero rows, whose score 0 the clamp below
+        // keeps finite.
+        if constexpr (DMA) {
+          if (j0 + 32 * c2 + 32 > N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (j0 + 32 * c2 + 8 * g + 4 * h + r >= N)
+#pragma unroll
+                for (int nb = 0; nb < QB; ++nb) s[h][nb][r] = kNegInf;
+          }
+        }
         // P is clamped to [0, 1] (the exp's output modifier, no extra
         // instruction).  A real key has P = exp(S - LSE) <= 1 already; a key
-        // past N (zero rows of K and V) has score 0 and P = exp(-LSE), which
+        // past N with a zero K row has score 0 and P = exp(-LSE), which
         // for a query with a very negative LSE overflows the operand type,
         // and inf times its zero K row would be NaN.  Clamped, its dS^T stays
         // finite and meets only zeros.
@@ -705,17 +755,21 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
       for (int db = 0; db < DK / 16; ++db) {
         Frag<T> a;
-        frag_ch(a, nat, SKV::LDN, 16 * db, 32 * c2);
+        frag_ch(a, chunk(nat, c2), LDN, 16 * db, ckey(c2));
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) mma(dqacc[db][nb], a, dsf[nb]);
       }
     }
 
-    if (kt + 1 < nkt) {
-      T* nx = smem + ((kt + 1) & 1) * BUF;
-      sk.store(nx, tid);
+    if constexpr (DMA) {
+      barrier_vmcnt<0>();  // this wave's loads of the next tile landed, then everyone's
+    } else {
+      if (kt + 1 < nkt) {
+        T* nx = smem + ((kt + 1) & 1) * BUF;
+        sk.store(nx, tid);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   auto epilogue = [&](auto accum) {
@@ -752,7 +806,7 @@ __global__ __launch_bounds__(NW * 64) void psa_bwd_fused_kernel(
     T* __restrict__ dpk, int N, int n_ktiles, int n_qtiles, int n_kblocks, int n_qblocks, float c, float scale,
     const PackView pv) {
   constexpr int S1 = DkdvShape<T, DK, DV, KB, NW, BMQ>::SMEM, S2 = DqShape<T, DK, DV, QB, NW, BN>::SMEM;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S1 > S2 ? S1 : S2];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S1 > S2 ? S1 : S2];
   const int b = block_id();
   if (b < n_kblocks)
     bwd_dkdv_body<T, DK, DV, KB, NW, BMQ, VECOK, DEEP>(qkv, dO, nl, nd, dpk, N, n_ktiles, c, scale, pv,
