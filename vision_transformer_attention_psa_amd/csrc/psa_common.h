@@ -394,11 +394,11 @@ __device__ __forceinline__ void barrier_vmcnt() {
 // never read).  Each of the NW waves owns L 1 KB loads of 64 slots (wv is
 // wave-uniform) and issues those of them that exist.  Rows [0, SPLIT) start
 // at element lo_off of the base pointer, rows [SPLIT, C) at hi_off, both in
-// rows of ld.
-// Chunks past the row's end are loaded from its last full chunk (ld - 8):
-// their values are finite data of the same row, and the caller gives those
-// tokens zero weight.
-template <typename T, int C, int BT, int NW, int SPLIT>
+// rows of ld.  A lane keeps one offset per load (its chunk at token 0); a
+// tile that reaches past ld recomputes the chunk from the lane and loads
+// chunks past the row's end from its last full chunk (ld - 8): finite data
+// of the same row, to which the caller gives zero weight.
+template <typename T, int C, int BT, int NW, int SPLIT = C>
 struct DmaStage {
   static_assert(is_16bit<T>(), "16-bit element type");
   static constexpr int TC = BT / 8, SLOTS = C * (TC + 1), LOADS = (SLOTS + 63) / 64;
@@ -406,28 +406,38 @@ struct DmaStage {
   static constexpr int BYTES = LOADS * 1024;       // LDS bytes of one stage
   static constexpr int ELEMS = BYTES / (int)sizeof(T);
   static_assert(BYTES >= C * nat_pitch<T>(BT) * (int)sizeof(T), "stage holds the tile");
-  int off[L];  // this lane's element offset from the base pointer at token 0
-  int tok[L];  // its chunk's first token within the tile
+  int off[L];  // element offset of this lane's chunk at token 0 from the base pointer
 
+  // First token of the chunk that slot s loads, within the tile.
+  __device__ static __forceinline__ int chunk_tok(int s) {
+    if (s >= SLOTS) return 0;  // past the tile: row C - 1, chunk 0
+    const int c = s % (TC + 1);
+    return 8 * (c == TC ? TC - 1 : c);  // the pad loads the row's last chunk
+  }
   __device__ __forceinline__ void init(int wv, int lane, int lo_off, int hi_off, int ld) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int s = 64 * (wv * L + i) + lane;
-      int r = s / (TC + 1), c = s - r * (TC + 1);
-      if (r >= C) r = C - 1, c = 0;  // past the tile
-      if (c == TC) c = TC - 1;       // the row's pad
-      off[i] = (r < SPLIT ? lo_off + r * ld : hi_off + (r - SPLIT) * ld);
-      tok[i] = 8 * c;
+      const int r = s < SLOTS ? s / (TC + 1) : C - 1;
+      off[i] = (r < SPLIT ? lo_off + r * ld : hi_off + (r - SPLIT) * ld) + chunk_tok(s);
     }
   }
   // Loads of the tile at token j0 into the stage at `lds`.
-  __device__ __forceinline__ void issue(const T* base, int j0, int ld, const void* lds, int wv) const {
+  __device__ __forceinline__ void issue(const T* base, int j0, int ld, const void* lds, int wv, int lane) const {
     const unsigned char* st = (const unsigned char*)lds + wv * L * 1024;
+    if (j0 + BT <= ld) {  // every chunk inside the rows
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      if (LOADS % NW != 0 && wv * L + i >= LOADS) break;
-      const int j = min(j0 + tok[i], ld - 8);
-      lds_dma16(base + off[i] + j, st + i * 1024);
+      for (int i = 0; i < L; ++i) {
+        if (LOADS % NW != 0 && wv * L + i >= LOADS) break;
+        lds_dma16(base + off[i] + j0, st + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        if (LOADS % NW != 0 && wv * L + i >= LOADS) break;
+        const int tok = chunk_tok(64 * (wv * L + i) + lane);
+        lds_dma16(base + off[i] - tok + min(j0 + tok, ld - 8), st + i * 1024);
+      }
     }
   }
 };

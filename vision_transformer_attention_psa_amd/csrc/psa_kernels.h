@@ -110,7 +110,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
   const int wv = __builtin_amdgcn_readfirstlane(w);
   if constexpr (DMA) {
     dst.init(wv, lane, DK * ld, pv.voff * ld, ld);
-    dst.issue(Qg, 0, ld, smem, wv);
+    dst.issue(Qg, 0, ld, smem, wv, lane);
     barrier_vmcnt<0>();
   } else {
     st.load(KVg, Vg, ld, N, 0, tid);
@@ -140,7 +140,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
     if (kt + 1 < nkt) {
       // the other stage was last read before the previous iteration's barrier
       if constexpr (DMA)
-        dst.issue(Qg, (kt + 1) * BN, ld, smem + ((kt + 1) & 1) * BUF, wv);
+        dst.issue(Qg, (kt + 1) * BN, ld, smem + ((kt + 1) & 1) * BUF, wv, lane);
       else
         st.load(KVg, Vg, ld, N, (kt + 1) * BN, tid);
     }
@@ -355,10 +355,17 @@ __global__ __launch_bounds__(256) void psa_pad_rows_kernel(const T* __restrict__
 template <typename T, int DK, int DV, int KB, int NW, int BMQ>
 struct DkdvShape {
   static constexpr int KW = 16 * KB, BNK = NW * KW, NT = NW * 64;
-  // Q|dO streamed tile and K|V stationary tile, both channel-major.
+  // Q|dO streamed tile and K|V stationary tile, both channel-major.  16-bit
+  // types stream Q and dO by direct loads where rows are 16-byte aligned
+  // (DQP, DGP: the Q rows, then the dO rows from a 1 KB boundary, each in
+  // the layout of the register staging SQG); a stage has room for either.
+  using T16 = std::conditional_t<is_16bit<T>(), T, bf16>;
   using SQG = Stager<T, DK + DV, BMQ, NT, true, DK>;
+  using DQP = DmaStage<T16, DK, BMQ, NW>;
+  using DGP = DmaStage<T16, DV, BMQ, NW>;
   using SKV = Stager<T, DK + DV, BNK, NT, true, DK>;
-  static constexpr int TILE = SQG::NAT_ELEMS;
+  static constexpr int DTILE = DQP::ELEMS + DGP::ELEMS;
+  static constexpr int TILE = is_16bit<T>() && DTILE > SQG::NAT_ELEMS ? DTILE : (int)SQG::NAT_ELEMS;
   static constexpr int QG_BYTES = 2 * TILE * (int)sizeof(T) + 4 * BMQ * (int)sizeof(float);
   static_assert(2 * TILE * sizeof(T) % 16 == 0, "statistics must be 16-byte aligned");
   static constexpr int KV_BYTES = SKV::NAT_ELEMS * (int)sizeof(T);
@@ -378,8 +385,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   static_assert(BMQ <= NT, "one statistics entry per thread");
   using SQG = Stager<T, DK + DV, BMQ, NT, VECOK, DK>;
   using SKV = Stager<T, DK + DV, BNK, NT, VECOK, DK>;
-  constexpr int TILE = SQG::NAT_ELEMS;
-  static_assert(TILE == Shape::TILE, "tile layout");
+  // Direct loads for the streamed tiles except in the two-deep register
+  // prefetch (DEEP), which keeps register staging.
+  constexpr bool DMA = VECOK && is_16bit<T>() && !DEEP;
+  using DQP = typename Shape::DQP;
+  using DGP = typename Shape::DGP;
+  constexpr int TILE = Shape::TILE, LDN = SQG::LDN;
+  constexpr int GOFF = DMA ? (int)DQP::ELEMS : DK * LDN;  // where the dO rows of a stage start
   T* smem = (T*)smem_raw;
   float* snl = (float*)(smem_raw + 2 * TILE * sizeof(T));  // [2][BMQ], then snd [2][BMQ]
   float* snd = snl + 2 * BMQ;
@@ -427,13 +439,32 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   }
 
   SQG sg;
-  sg.load(Qg, dOg, ld, N, 0, tid);
-  sg.store(smem, tid);
+  DQP dqp;
+  DGP dgp;
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  // Direct loads of query tile qt's Q and dO rows into a stage.
+  auto issue_tile = [&](int qt, T* stage) {
+    if constexpr (DMA) {
+      dqp.issue(Qg, qt * BMQ, ld, stage, wv, lane);
+      dgp.issue(dOg, qt * BMQ, ld, stage + GOFF, wv, lane);
+    }
+  };
+  if constexpr (DMA) {
+    dqp.init(wv, lane, 0, 0, ld);
+    dgp.init(wv, lane, 0, 0, ld);
+    issue_tile(0, smem);
+  } else {
+    sg.load(Qg, dOg, ld, N, 0, tid);
+    sg.store(smem, tid);
+  }
   for (int q = tid; q < BMQ; q += NT) {  // padding rows: P = 0
     snl[q] = q < N ? nlq[q] : kNegInf;
     snd[q] = q < N ? ndq[q] : 0.f;
   }
-  __syncthreads();
+  if constexpr (DMA)
+    barrier_vmcnt<0>();
+  else
+    __syncthreads();
 
   // DEEP: the two thread halves take turns, each keeping one tile in flight
   // in its registers from the top of iteration qt to the end of qt + 1: a
@@ -447,7 +478,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   auto load_tile = [&](int qt, int lt) {  // rows and statistics of query tile qt (lt = thread index)
     if constexpr (DEEP)
       sh.load(Qg, dOg, ld, N, qt * BMQ, lt);
-    else
+    else if constexpr (!DMA)
       sg.load(Qg, dOg, ld, N, qt * BMQ, lt);
     const int q = qt * BMQ + lt;
     pnl = kNegInf, pnd = 0.f;
@@ -469,8 +500,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
     // registers; they reach LDS after this tile's MFMAs.
     if constexpr (DEEP) {
       if (qt + 2 < nqt && half == cur) load_tile(qt + 2, htid);
-    } else {
-      if (qt + 1 < nqt) load_tile(qt + 1, tid);
+    } else if (qt + 1 < nqt) {
+      // the other stage was last read before the previous iteration's barrier
+      issue_tile(qt + 1, smem + (cur ^ 1) * TILE);
+      load_tile(qt + 1, tid);
     }
 
 #pragma unroll
@@ -494,14 +527,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
-          frag_tok<DK, true>(a, nat, SQG::LDN, 32 * c2, h, 32 * kc);
+          frag_tok<DK, true>(a, nat, LDN, 32 * c2, h, 32 * kc);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(s[h][kb], a, kf[kb][kc]);
         }
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
           Frag<T> a;
-          frag_tok<DV, true>(a, nat + DK * SQG::LDN, SQG::LDN, 32 * c2, h, 32 * cc);
+          frag_tok<DV, true>(a, nat + GOFF, LDN, 32 * c2, h, 32 * cc);
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(dp[h][kb], a, vf[kb][cc]);
         }
@@ -525,14 +558,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
       for (int cb = 0; cb < DV / 16; ++cb) {
         Frag<T> a;
-        frag_ch(a, nat, SQG::LDN, DK + 16 * cb, 32 * c2);
+        frag_ch(a, nat + GOFF, LDN, 16 * cb, 32 * c2);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mma(dvacc[cb][kb], a, pf[kb]);
       }
 #pragma unroll
       for (int db = 0; db < DK / 16; ++db) {
         Frag<T> a;
-        frag_ch(a, nat, SQG::LDN, 16 * db, 32 * c2);
+        frag_ch(a, nat, LDN, 16 * db, 32 * c2);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mma(dkacc[db][kb], a, dsf[kb]);
       }
@@ -543,14 +576,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
       const int lt = DEEP ? htid : tid;
       if constexpr (DEEP)
         sh.store(nx, lt);
-      else
+      else if constexpr (!DMA)
         sg.store(nx, lt);
       if (lt < BMQ) {
         snl[(cur ^ 1) * BMQ + lt] = pnl;
         snd[(cur ^ 1) * BMQ + lt] = pnd;
       }
     }
-    __syncthreads();
+    if constexpr (DMA)
+      barrier_vmcnt<0>();  // this wave's loads of the next tile landed, then everyone's
+    else
+      __syncthreads();
   }
 
   auto epilogue = [&](auto accum) {
@@ -665,7 +701,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   auto issue = [&](int j0, T* stage) {
     if constexpr (DMA) {
 #pragma unroll
-      for (int u = 0; u < NSUB; ++u) dkv.issue(Qg, j0 + u * SUB, ld, stage + u * DKV::ELEMS, wv);
+      for (int u = 0; u < NSUB; ++u) dkv.issue(Qg, j0 + u * SUB, ld, stage + u * DKV::ELEMS, wv, lane);
     }
   };
   // Where chunk c2's 32 keys sit: sub-tile c2 / (SUB / 32) of a direct-load
