@@ -109,6 +109,10 @@ EDGE = [
     (inputs.BF16, 32, 64, 1, 2, 1599),
     (inputs.BF16, 64, 64, 1, 1, 6399),
     (inputs.F16, 64, 64, 1, 1, 6398),
+    # padded rows whose last tile reaches past the row stride at the dk = 64 tile shapes
+    # (64-key forward tiles, 64-query dK/dV tiles, 128-key dQ stages of two 64-key halves)
+    (inputs.BF16, 64, 64, 1, 2, 1003),
+    (inputs.F16, 64, 64, 2, 1, 2001),
 ]
 
 
