@@ -77,7 +77,11 @@ typedef enum {
  *   o    out  [B, heads, dv, N], dtype
  *   lse  out  [B, heads, N], float32 (natural log of sum_j exp(s q_i.k_j))
  *   scale     softmax scale s, finite and > 0 (usually 1/sqrt(dk))
- * Scratch: none.
+ * Scratch: none for float32, or N a multiple of 8, or N < 96.  Otherwise
+ * (16-bit rows that 16-byte loads cannot address) qkv is first copied into
+ * rows of N8 = N rounded up to 8, zero past N: 2*B*heads*(2dk+dv)*N8 bytes
+ * from the per-(device, stream) buffer described under psa_attn_bwd, with
+ * the same rules under graph capture.
  */
 int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N,
                  int dk, int dv, float scale, int dtype, void* stream);
@@ -94,7 +98,11 @@ int psa_attn_fwd(const void* qkv, void* o, float* lse, int B, int heads, int N,
  *                  run to run; no floating-point atomics)
  * Scratch: 8*B*heads*N bytes of device memory from a grow-only buffer the
  * library keeps per (device, stream) until the process ends; the first call
- * on a stream (or a larger one) allocates it with hipMalloc.  Under HIP graph
+ * on a stream (or a larger one) allocates it with hipMalloc.  For 16-bit
+ * rows with N >= 96 not a multiple of 8, qkv, o and dO are first copied
+ * into rows of N8 = N rounded up to 8 (zero past N), which adds
+ * 2*B*heads*(2dk+2dv)*N8 bytes (each of the four parts rounded up to 256
+ * bytes).  Under HIP graph
  * capture: make one uncaptured call of at least the captured size on that
  * stream first (capture cannot allocate), and do not make a larger call on
  * that stream while the graph is in use (growing frees the buffer the graph
@@ -108,7 +116,9 @@ int psa_attn_bwd(const void* qkv, const void* o, const float* lse, const void* d
  * psa_attn_bwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments, kernels and results (bitwise identical to
- * psa_attn_bwd), but its scratch is a fixed 16 MiB device array compiled
+ * psa_attn_bwd; it reads ragged rows in place instead of copying them into
+ * padded ones, which changes no bit), but its scratch is a fixed 16 MiB
+ * device array compiled
  * into the library, one copy per GPU, held until the process ends.  It
  * calls no hipMalloc, hipFree or other allocating routine.
  * Limit: B*heads*N <= 2097152 (2^21 queries, two fp32 statistics each);
@@ -191,8 +201,11 @@ int psa_merge_bwd(const void* d_merged, void* d_lo, void* d_hi, int B, int heads
  * and the sum over (b, n) for dw runs in a fixed order, so results are
  * bitwise reproducible.  cin and cout must be multiples of 128 (else
  * PSA_ERR_UNSUPPORTED); N is arbitrary.  dx and dw must not overlap the
- * inputs or each other.  Scratch: when the dw sum is split, S*cout*cin*4
- * bytes (S <= 64) from the same per-(device, stream) buffer as psa_attn_bwd.
+ * inputs or each other.  Scratch, from the same per-(device, stream)
+ * buffer as psa_attn_bwd: when the dw sum is split, S*cout*cin*4 bytes
+ * (S <= 64); for 16-bit N not a multiple of 8, zero-padded copies of x and
+ * dy with rows of N rounded up to 8 as well (each part rounded up to 256
+ * bytes).
  */
 int psa_qkv_conv_bwd(const void* x, const void* w, const void* dy, void* dx, void* dw, int B, int cin,
                      int cout, int N, int dtype, void* stream);
