@@ -128,6 +128,35 @@ def test_edge_shapes(dtype, dk, dv, B, H, N):
     assert max(err.values()) <= TOL[dtype], err
 
 
+def _random_shapes(count, seed=2024):
+    """A fixed, seeded draw of shapes across the compiled (dk, dv) pairs, both
+    16-bit types and ragged lengths up to about 2100 (every load width, the
+    padded copies, partial last tiles of every tile width), one or two slices
+    each so that the oracle stays fast."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pairs = [(32, 32), (32, 64), (64, 32), (64, 64), (64, 128), (128, 128)]
+    out = []
+    for _ in range(count):
+        dk, dv = pairs[rng.integers(len(pairs))]
+        dtype = inputs.BF16 if rng.integers(2) else inputs.F16
+        n = int(rng.integers(1, 2101)) if rng.integers(3) else int(8 * rng.integers(1, 263))
+        B, H = (1, 2) if rng.integers(2) else (2, 1)
+        out.append((dtype, dk, dv, B, H, n))
+    return out
+
+
+@pytest.mark.parametrize("dtype,dk,dv,B,H,N", _random_shapes(40))
+def test_random_shapes(dtype, dk, dv, B, H, N):
+    wl = inputs.Workload(f"rand_{dtype}_{dk}_{dv}_{B}x{H}_n{N}", B=B, heads=H, H=N, W=1, dk=dk,
+                         dv=dv, dtype=dtype, seed=300 + N)
+    x = inputs.make_inputs(wl)
+    got = run_chained(x)
+    ref = orc.forward_backward(x.qkv, x.dO, dk, dv, wl.scale)
+    err = errors(wl, got, ref)
+    print(wl.name, {k: f"{v:.2e}" for k, v in err.items()}, flush=True)
+    assert max(err.values()) <= TOL[dtype], err
+
+
 # More tiles than the GPU holds workgroups at once (two per CU on 256 CUs),
 # so workgroups run in several rounds; ragged and 16-byte-aligned N.
 MANY_TILES = [
