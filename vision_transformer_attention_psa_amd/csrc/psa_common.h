@@ -371,6 +371,13 @@ __device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
   const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(a) : "memory");
 }
+// The same load addressed as a wave-uniform base (SGPRs) plus this lane's
+// byte offset, which the hardware zero-extends: no per-lane 64-bit address
+// arithmetic.
+__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, const void* lds) {
+  const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(a) : "memory");
+}
 
 // Workgroup barrier once this wave's LDS reads and all but its last NV
 // vector-memory operations have completed (lgkmcnt 0, vmcnt NV; gfx9
@@ -406,7 +413,7 @@ struct DmaStage {
   static constexpr int BYTES = LOADS * 1024;       // LDS bytes of one stage
   static constexpr int ELEMS = BYTES / (int)sizeof(T);
   static_assert(BYTES >= C * nat_pitch<T>(BT) * (int)sizeof(T), "stage holds the tile");
-  int off[L];  // element offset of this lane's chunk at token 0 from the base pointer
+  unsigned off[L];  // byte offset of this lane's chunk at token 0 from the base pointer
 
   // First token of the chunk that slot s loads, within the tile.
   __device__ static __forceinline__ int chunk_tok(int s) {
@@ -419,24 +426,29 @@ struct DmaStage {
     for (int i = 0; i < L; ++i) {
       const int s = 64 * (wv * L + i) + lane;
       const int r = s < SLOTS ? s / (TC + 1) : C - 1;
-      off[i] = (r < SPLIT ? lo_off + r * ld : hi_off + (r - SPLIT) * ld) + chunk_tok(s);
+      const int e = (r < SPLIT ? lo_off + r * ld : hi_off + (r - SPLIT) * ld) + chunk_tok(s);
+      off[i] = (unsigned)e * (unsigned)sizeof(T);
     }
   }
-  // Loads of the tile at token j0 into the stage at `lds`.
+  // Loads of the tile at token j0 into the stage at `lds`.  Offsets are
+  // below 2^32 bytes: the callers' tiles lie within fewer than 2^31 elements
+  // of `base`.
   __device__ __forceinline__ void issue(const T* base, int j0, int ld, const void* lds, int wv, int lane) const {
     const unsigned char* st = (const unsigned char*)lds + wv * L * 1024;
     if (j0 + BT <= ld) {  // every chunk inside the rows
+      const T* tile = base + j0;
 #pragma unroll
       for (int i = 0; i < L; ++i) {
         if (LOADS % NW != 0 && wv * L + i >= LOADS) break;
-        lds_dma16(base + off[i] + j0, st + i * 1024);
+        lds_dma16(tile, off[i], st + i * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
         if (LOADS % NW != 0 && wv * L + i >= LOADS) break;
         const int tok = chunk_tok(64 * (wv * L + i) + lane);
-        lds_dma16(base + off[i] - tok + min(j0 + tok, ld - 8), st + i * 1024);
+        const long long d = (long long)(min(j0 + tok, ld - 8) - tok) * (long long)sizeof(T);
+        lds_dma16((const unsigned char*)base + off[i] + d, st + i * 1024);
       }
     }
   }
