@@ -243,6 +243,13 @@ int check_launch(const char* what) {
 }
 
 template <typename T> constexpr bool vec_ok(int N) { return N % (16 / (int)sizeof(T)) == 0; }
+// The aligned attention instances (16-byte loads; for 16-bit types direct
+// loads into LDS) address a slice with 32-bit element offsets, and the direct
+// loads with 32-bit byte offsets from a scalar base: a slice of 2^31 bytes or
+// more goes to the instances with 64-bit offsets.
+template <typename T> bool aligned_ok(const psa::PackView& pv) {
+  return vec_ok<T>(pv.ld) && (long long)pv.cs * pv.ld * (long long)sizeof(T) < INT32_MAX;
+}
 
 // Inputs whose rows (N tokens of a 16-bit type) are not a multiple of 8 are
 // staged once into zero-padded rows of N rounded up to 8, so that the
@@ -287,9 +294,7 @@ int run_fwd(const void* qkv, void* o, float* lse, int BH, int N, float scale, ps
   const float c = scale * psa::kLog2e;
   const dim3 g((unsigned)grid), b(C::FWD_NW * 64);
   TimedLaunch tl(K_FWD, st);
-  // The aligned instance (16-byte loads; for 16-bit types direct loads into
-  // LDS) addresses a slice with 32-bit element offsets.
-  if (vec_ok<T>(pv.ld) && (long long)pv.cs * pv.ld < INT32_MAX)
+  if (aligned_ok<T>(pv))
     hipLaunchKernelGGL((psa::psa_fwd_kernel<T, DK, DV, C::FWD_QB, C::FWD_NW, C::FWD_BN, true, C::FWD_OCC>), g, b, 0, st,
                        (const T*)qkv, (T*)o, lse, N, nqt, (int)grid, c, pv);
   else
@@ -334,8 +339,7 @@ int run_bwd(const void* qkv, const void* o, const float* lse, const void* dO, vo
   {
     TimedLaunch tl(K_MAIN, st);
     const dim3 grid((unsigned)(nkb + nqb)), block(NW * 64);
-    // as in the forward: 32-bit element offsets within a slice
-    if (vec_ok<T>(pv.ld) && (long long)pv.cs * pv.ld < INT32_MAX)
+    if (aligned_ok<T>(pv))
       hipLaunchKernelGGL(
           (psa::psa_bwd_fused_kernel<T, DK, DV, C::DKDV_KB, C::DKDV_BMQ, C::DQ_QB, C::DQ_BN, NW, true, C::DKDV_DEEP>), grid, block, 0,
           st, (const T*)qkv, (const T*)dO, nl, nd, (T*)dpk, N, nkt, nqt, nkb, nqb, c, scale, pv);

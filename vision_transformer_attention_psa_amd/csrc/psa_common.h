@@ -430,9 +430,9 @@ struct DmaStage {
       off[i] = (unsigned)e * (unsigned)sizeof(T);
     }
   }
-  // Loads of the tile at token j0 into the stage at `lds`.  Offsets are
-  // below 2^32 bytes: the callers' tiles lie within fewer than 2^31 elements
-  // of `base`.
+  // Loads of the tile at token j0 into the stage at `lds`.  The callers keep
+  // every tile within 2^31 bytes of `base`, so each byte offset is the same
+  // read as signed or unsigned.
   __device__ __forceinline__ void issue(const T* base, int j0, int ld, const void* lds, int wv, int lane) const {
     const unsigned char* st = (const unsigned char*)lds + wv * L * 1024;
     if (j0 + BT <= ld) {  // every chunk inside the rows
