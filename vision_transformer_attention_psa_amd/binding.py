@@ -25,7 +25,7 @@ EXPORTS = ("psa_attn_fwd", "psa_attn_bwd", "psa_attn_bwd_noalloc", "psa_attn_fwd
            "psa_channel_cat_bwd", "psa_attn_supported", "psa_last_error",
            "psa_attn_version", "psa_attn_timing_enable", "psa_attn_timing_read",
            "psa_attn_timing_reset")
-TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "bwd_dq", "conv_dx", "conv_dw", "cat", "merge_fwd", "merge_bwd")
+TIMING_SLOTS = ("fwd", "bwd_pre", "bwd_main", "reserved", "conv_dx", "conv_dw", "cat", "merge_fwd", "merge_bwd")
 
 _lib = None
 

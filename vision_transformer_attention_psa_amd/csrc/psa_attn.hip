@@ -117,10 +117,11 @@ template <int DK, int DV> struct TilesNarrow<float, DK, DV> : TilesWide<float, D
 
 // ------------------------------------------------------- per-kernel timing
 // Slots: forward; D/LSE preprocessing; the backward GEMM launch (dK/dV and
-// dQ in one grid); the dQ reduction; the 1x1-conv backward's
-// dx GEMM; its dw GEMM (with the split reduction); the channel-cat slice copy;
-// the PSA merge forward and backward copies.
-enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_DQ = 3, K_CONV_DX = 4, K_CONV_DW = 5, K_CAT = 6, K_MERGE_FWD = 7,
+// dQ in one grid); a reserved slot with no kernel (kept so that the slot
+// numbers of the ABI stay fixed); the 1x1-conv backward's dx GEMM; its dw
+// GEMM (with the split reduction); the channel-cat slice copy; the PSA merge
+// forward and backward copies.
+enum { K_FWD = 0, K_PRE = 1, K_MAIN = 2, K_RESERVED = 3, K_CONV_DX = 4, K_CONV_DW = 5, K_CAT = 6, K_MERGE_FWD = 7,
        K_MERGE_BWD = 8 };
 
 struct Timing {
