@@ -193,7 +193,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
           const float alpha = fast_exp2(m[nb] - mn);
           m[nb] = mn;
           thr[nb] = (mn + kRescaleSlack) * cinv;
-          lacc[nb] *= alpha;
+          lacc[nb][0] *= alpha;  // only row 0 of the ones-product is read (epilogue)
 #pragma unroll
           for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] *= alpha;
         }
