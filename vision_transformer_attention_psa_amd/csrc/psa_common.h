@@ -236,7 +236,13 @@ __device__ __forceinline__ u32x4 load8_funnel(const void* p, int avail) {
 //   fp32: 16-byte chunks (4 tokens of one row).
 // VECOK: ld is a multiple of the 16-byte vector, so every chunk is aligned;
 // a chunk that crosses N (padded rows only) brings the row's zero padding.
-template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT>
+// CL (clamp, 16-byte loads only): instead of zeros, chunks past the rows'
+// end repeat the row's last full chunk and lanes past the tile repeat its
+// last block, so that no lane needs zeroing or a branch.  For streamed tiles
+// whose tokens past N get zero weight anyway (the dK/dV body's queries,
+// which carry -inf statistics); tokens that are a contraction index (the
+// conv's dw) or that must be zero rows keep the default.
+template <typename T, int C, int BT, int NT, bool VECOK, int SPLIT, bool CL = false>
 struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   static_assert(is_16bit<T>(), "16-bit element type");
   static constexpr int CG = C / 4, TC = BT / 8, NB = CG * TC, PER = (NB + NT - 1) / NT;
@@ -262,15 +268,20 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   __device__ __forceinline__ void load_w(const T* __restrict__ lo, const T* __restrict__ hi, int ld, int N, int j0,
                                          int tid) {
     constexpr int TPL = W / 2;  // tokens per load
+    constexpr bool CLAMP = W == 16 && CL;  // see CL above
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int q = tid + u * NT;
+      const int q = CLAMP && NB % NT != 0 ? min(tid + u * NT, NB - 1) : tid + u * NT;
       const int tc = blk_tc(q), cg = blk_cg(q);
       const int j = j0 + 8 * tc;
       const bool live = NB % NT == 0 || q < NB;
       const T* base = 4 * cg < SPLIT ? lo + (size_t)(4 * cg) * ld : hi + (size_t)(4 * cg - SPLIT) * ld;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if constexpr (CLAMP) {
+          r[u][i] = *(const u32x4*)(base + (size_t)i * ld + min(j, ld - 8));
+          continue;
+        }
         r[u][i] = u32x4{0u, 0u, 0u, 0u};
         if (!live) continue;
         const T* p = base + (size_t)i * ld + j;
@@ -321,8 +332,8 @@ struct Stager {  // 16-bit element types (the fp32 specialisation follows)
   }
 };
 
-template <int C, int BT, int NT, bool VECOK, int SPLIT>
-struct Stager<float, C, BT, NT, VECOK, SPLIT> {
+template <int C, int BT, int NT, bool VECOK, int SPLIT, bool CL>
+struct Stager<float, C, BT, NT, VECOK, SPLIT, CL> {  // zero fill in every case
   static constexpr int CPR = BT / 4, CHUNKS = C * CPR, PER = (CHUNKS + NT - 1) / NT;
   static constexpr int LDN = nat_pitch<float>(BT);
   static constexpr int NAT_ELEMS = C * LDN;

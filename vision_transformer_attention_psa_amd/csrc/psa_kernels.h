@@ -470,7 +470,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // in its registers from the top of iteration qt to the end of qt + 1: a
   // prefetch distance of two tiles, at the register cost of one wherever a
   // tile needs no more than half the threads.
-  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK>;
+  using SQH = Stager<T, DK + DV, BMQ, NT / 2, VECOK, DK, true>;  // queries past N weigh 0: clamped loads
   static_assert(!DEEP || BMQ <= NT / 2, "one statistics entry per thread of a half");
   const int half = tid >= NT / 2, htid = tid - half * (NT / 2);
   SQH sh;
