@@ -195,7 +195,17 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
           thr[nb] = (mn + kRescaleSlack) * cinv;
           lacc[nb][0] *= alpha;  // only row 0 of the ones-product is read (epilogue)
 #pragma unroll
-          for (int cb = 0; cb < DV / 16; ++cb) oacc[cb][nb] *= alpha;
+          for (int cb = 0; cb < DV / 16; ++cb) {
+            // With one query block, element by element: the vector form made
+            // the compiler copy an accumulator at every iteration's end (and
+            // the element form costs the wider tiles registers).
+            if constexpr (QB == 1) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) oacc[cb][nb][r] *= alpha;
+            } else {
+              oacc[cb][nb] *= alpha;
+            }
+          }
         }
       }
       Frag<T> pf[QB];
