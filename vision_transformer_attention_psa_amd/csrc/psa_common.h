@@ -383,8 +383,8 @@ __device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(a) : "memory");
 }
 // The same load addressed as a wave-uniform base (SGPRs) plus this lane's
-// byte offset, which the hardware zero-extends: no per-lane 64-bit address
-// arithmetic.
+// 32-bit byte offset: no per-lane 64-bit address arithmetic.  Callers keep
+// the offset below 2^31, where a signed and an unsigned reading agree.
 __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, const void* lds) {
   const unsigned a = (unsigned)(size_t)(const __attribute__((address_space(3))) void*)lds;
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(a) : "memory");
