@@ -144,6 +144,10 @@ EDGE = [
     (inputs.BF16, 64, 64, 2, 1, 384),
     (inputs.F16, 32, 64, 1, 1, 320),
     (inputs.F32, 32, 64, 1, 1, 36),
+    # its clamped loads: a last query tile that reaches past the (padded) rows' end,
+    # N = 1003 (rows of 1008) and N = 777 (rows of 784), both 16-bit types
+    (inputs.BF16, 32, 64, 2, 2, 1003),
+    (inputs.F16, 32, 32, 1, 3, 777),
     # rows that are not 16-byte aligned: below the staging length the kernels load them
     # with 8-, 4- or 2-byte loads or funnel shifts (N % 8 = 4, 6, odd); from it on they
     # are staged into zero-padded rows, also at the large-N tile shapes
