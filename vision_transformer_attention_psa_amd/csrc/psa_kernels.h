@@ -398,6 +398,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // Direct loads for the streamed tiles except in the two-deep register
   // prefetch (DEEP), which keeps register staging.
   constexpr bool DMA = VECOK && is_16bit<T>() && !DEEP;
+  // Wave priority raised over the MFMA blocks and lowered over the softmax
+  // (both bodies, 16-bit, dk >= 64): the N = 6400 backward 1016-1017 vs
+  // 1021-1024 us on one box and 974-975 vs 980-981 us on another; at dk = 32
+  // it cost 10 % at N = 400, and in the forward 1.5 %.
+  constexpr bool PRIO = is_16bit<T>() && DK >= 64;
   using DQP = typename Shape::DQP;
   using DGP = typename Shape::DGP;
   constexpr int TILE = Shape::TILE, LDN = SQG::LDN;
@@ -534,6 +539,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
           s[h][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[h][kb] = nd[h];
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
@@ -548,6 +554,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) mma(dp[h][kb], a, vf[kb][cc]);
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -565,6 +572,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
         acc_to_frag(pf[kb], s[0][kb], s[1][kb]);
         acc_to_frag(dsf[kb], dp[0][kb], dp[1][kb]);
       }
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cb = 0; cb < DV / 16; ++cb) {
         Frag<T> a;
@@ -579,6 +587,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mma(dkacc[db][kb], a, dsf[kb]);
       }
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     if (qt + 1 < nqt && (!DEEP || half != cur)) {
@@ -656,6 +665,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
   constexpr bool DMA = VECOK && is_16bit<T>();
+  constexpr bool PRIO = is_16bit<T>() && DK >= 64;  // as in the dK/dV body
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK>;
   using DKV = typename Shape::DKV;
   using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK>;
@@ -754,6 +764,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
           s[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[h][nb] = f32x4{nd[nb], nd[nb], nd[nb], nd[nb]};
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
@@ -768,6 +779,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         // Keys past N: direct loads leave other tokens' (finite) values in
         // their K and V rows, so their scores get zero weight here; the
         // register staging leaves zero rows, whose score 0 the clamp below
@@ -798,6 +810,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
       Frag<T> dsf[QB];
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) acc_to_frag(dsf[nb], dp[0][nb], dp[1][nb]);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int db = 0; db < DK / 16; ++db) {
         Frag<T> a;
@@ -805,6 +818,7 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) mma(dqacc[db][nb], a, dsf[nb]);
       }
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     if constexpr (DMA) {
