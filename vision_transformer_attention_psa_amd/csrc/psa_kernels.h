@@ -398,10 +398,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // Direct loads for the streamed tiles except in the two-deep register
   // prefetch (DEEP), which keeps register staging.
   constexpr bool DMA = VECOK && is_16bit<T>() && !DEEP;
-  // Wave priority raised over the MFMA blocks and lowered over the softmax
-  // (both bodies, 16-bit, dk >= 64): the N = 6400 backward 1016-1017 vs
-  // 1021-1024 us on one box and 974-975 vs 980-981 us on another; at dk = 32
-  // it cost 10 % at N = 400, and in the forward 1.5 %.
+  // Wave priority raised over the score MFMAs (S and dP) and lowered for the
+  // softmax (both bodies, 16-bit, dk >= 64): the N = 6400 backward 985-987
+  // vs 989-991 us with it raised over every MFMA block too, and about 1 %
+  // below no raise at all; at dk = 32 it cost 10 % at N = 400, and in the
+  // forward 1.5 %.
   constexpr bool PRIO = is_16bit<T>() && DK >= 64;
   using DQP = typename Shape::DQP;
   using DGP = typename Shape::DGP;
@@ -572,7 +573,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
         acc_to_frag(pf[kb], s[0][kb], s[1][kb]);
         acc_to_frag(dsf[kb], dp[0][kb], dp[1][kb]);
       }
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cb = 0; cb < DV / 16; ++cb) {
         Frag<T> a;
@@ -587,7 +587,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) mma(dkacc[db][kb], a, dsf[kb]);
       }
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     if (qt + 1 < nqt && (!DEEP || half != cur)) {
@@ -810,7 +809,6 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
       Frag<T> dsf[QB];
 #pragma unroll
       for (int nb = 0; nb < QB; ++nb) acc_to_frag(dsf[nb], dp[0][nb], dp[1][nb]);
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int db = 0; db < DK / 16; ++db) {
         Frag<T> a;
@@ -818,7 +816,6 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) mma(dqacc[db][nb], a, dsf[nb]);
       }
-      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     if constexpr (DMA) {
