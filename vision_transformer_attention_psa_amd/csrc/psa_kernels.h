@@ -401,8 +401,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // Wave priority raised over the score MFMAs (S and dP) and lowered for the
   // softmax (both bodies, 16-bit, dk >= 64): the N = 6400 backward 985-987
   // vs 989-991 us with it raised over every MFMA block too, and about 1 %
-  // below no raise at all; at dk = 32 it cost 10 % at N = 400, and in the
-  // forward 1.5 %.
+  // below no raise at all; at dk = 32 it cost 3 % at N = 400 to 800, and in
+  // the forward 1.5 %.
   constexpr bool PRIO = is_16bit<T>() && DK >= 64;
   using DQP = typename Shape::DQP;
   using DGP = typename Shape::DGP;
