@@ -67,6 +67,10 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
                     int n_blocks, float c /* scale * log2(e) */, const PackView pv) {
   constexpr int QW = 16 * QB, BM = NW * QW, NT = NW * 64;
   constexpr int KC = Chunks<DK>::n;
+  // Wave priority raised over the score MFMAs and lowered for the softmax
+  // (16-bit, dk >= 64, wide tiles): N = 6400 383-384 vs 387-388 us; raised
+  // over the PV MFMAs as well it cost 1.5 %.
+  constexpr bool PRIO = is_16bit<T>() && DK >= 64 && QB > 1;
   static_assert(BN % 32 == 0 && DV % 16 == 0, "tile shape");
   // K|V tile, channel-major: K rows read as token rows for S^T, V rows as
   // channel rows for PV.  16-bit types with 16-byte rows (VECOK) bring it
@@ -153,6 +157,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int nb = 0; nb < QB; ++nb) s[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
@@ -161,6 +166,7 @@ void psa_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ o, float* __restr
           for (int nb = 0; nb < QB; ++nb) mma(s[h][nb], a, qf[nb][kc]);
         }
       }
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
       if (j0 + 32 * c2 + 32 > N) {  // keys past the end get zero weight
 #pragma unroll
         for (int h = 0; h < 2; ++h)
