@@ -405,10 +405,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const T* __restrict__ qkv, const T
   // prefetch (DEEP), which keeps register staging.
   constexpr bool DMA = VECOK && is_16bit<T>() && !DEEP;
   // Wave priority raised over the score MFMAs (S and dP) and lowered for the
-  // softmax (both bodies, 16-bit, dk >= 64): the N = 6400 backward 985-987
-  // vs 989-991 us with it raised over every MFMA block too, and about 1 %
-  // below no raise at all; at dk = 32 it cost 3 % at N = 400 to 800, and in
-  // the forward 1.5 %.
+  // softmax (16-bit, dk >= 64): the N = 6400 backward about 1 % faster than
+  // with no raise, and than with it raised over every MFMA block; in the dQ
+  // body as well it changed nothing (1002-1005 vs 1001-1002 us), in the dQ
+  // body alone it cost 1.3 %; at dk = 32 it cost 3 % at N = 400 to 800.
   constexpr bool PRIO = is_16bit<T>() && DK >= 64;
   using DQP = typename Shape::DQP;
   using DGP = typename Shape::DGP;
@@ -670,7 +670,6 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
   constexpr int KC = Chunks<DK>::n, CC = Chunks<DV>::n;
   static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
   constexpr bool DMA = VECOK && is_16bit<T>();
-  constexpr bool PRIO = is_16bit<T>() && DK >= 64;  // as in the dK/dV body
   using SKV = Stager<T, DK + DV, BN, NT, VECOK, DK>;
   using DKV = typename Shape::DKV;
   using SQG = Stager<T, DK + DV, BM, NT, VECOK, DK>;
@@ -769,7 +768,6 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
           s[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[h][nb] = f32x4{nd[nb], nd[nb], nd[nb], nd[nb]};
         }
-        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
           Frag<T> a;
@@ -784,7 +782,6 @@ __device__ __forceinline__ void bwd_dq_body(const T* __restrict__ qkv, const T* 
 #pragma unroll
           for (int nb = 0; nb < QB; ++nb) mma(dp[h][nb], a, gf[nb][cc]);
         }
-        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         // Keys past N: direct loads leave other tokens' (finite) values in
         // their K and V rows, so their scores get zero weight here; the
         // register staging leaves zero rows, whose score 0 the clamp below
