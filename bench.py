@@ -58,13 +58,14 @@ def hbm_bytes(wl, e: int) -> dict:
     }
 
 
-KERNEL_SOURCES = ("psa_kernels.h", "psa_common.h", "psa_attn.hip")
+KERNEL_SOURCES = ("psa_kernels.h", "psa_common.h", "psa_attn.hip", "../build.py")  # build.py: the compile flags
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_fingerprint() -> str:
-    """Hash of the HIP sources: counter-based traffic is reported only while it
-    was measured on exactly these kernels."""
+    """Hash of the HIP sources and of the build script (its compile flags):
+    counter-based traffic is reported only while it was measured on exactly
+    these kernels."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "vision_transformer_attention_psa_amd", "csrc", name), "rb") as f:
