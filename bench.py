@@ -58,7 +58,10 @@ def hbm_bytes(wl, e: int) -> dict:
     }
 
 
-KERNEL_SOURCES = ("psa_kernels.h", "psa_common.h", "psa_attn.hip", "../build.py")  # build.py: the compile flags
+# every kernel source of the traced run (the traffic summary lists the
+# convolution kernels too); build.py: the compile flags
+KERNEL_SOURCES = ("psa_kernels.h", "psa_common.h", "psa_attn.hip", "psa_conv_kernels.h", "psa_conv_wide.h",
+                  "psa_conv_wide.hip", "../build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

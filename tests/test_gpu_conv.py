@@ -30,6 +30,11 @@ SHAPES = [
     (inputs.BF16, 4, 512, 1536, 6399),
     (inputs.F16, 4, 384, 512, 6400),
     (inputs.BF16, 4, 384, 512, 6397),
+    # large-tile dw pipeline (cin a multiple of 256): a last token stage of
+    # 48 and of 8 tokens (the upper half-stage all past the row end), and
+    # rows padded to 1008 with a 48-token last stage
+    (inputs.F16, 4, 512, 1024, 6408),
+    (inputs.F16, 8, 512, 1024, 1001),
 ]
 
 

@@ -377,6 +377,10 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
   long long S = (2LL * cus) / tiles;
   S = std::min<long long>(S, std::max<long long>(1, nchunk / 4));
   S = std::max<long long>(1, std::min<long long>(S, 64));
+  // 16-bit types: the large-tile kernel when it applies (its own split count)
+  int S_pipe = 0;
+  if constexpr (psa::is_16bit<T>()) S_pipe = psa::conv_dw_pipe_splits(B, cin, cout, ld, cus);
+  if (S_pipe > 0) S = S_pipe;
   // one scratch buffer: dw's fp32 partials, then the padded x and dy
   const size_t pb = S > 1 ? round256((size_t)S * cout * cin * sizeof(float)) : 0;
   const size_t xb = ld != N ? round256((size_t)B * cin * ld * sizeof(T)) : 0;
@@ -415,7 +419,10 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
   if (rc != PSA_OK) return rc;
   TimedLaunch tl(K_CONV_DW, st);
   const int gw = (int)(tiles * S);
-  if (vec_ok<T>(ld))
+  if (S_pipe > 0) {
+    if constexpr (psa::is_16bit<T>())
+      psa::conv_dw_pipe_launch((const T*)x, (const T*)dy, (T*)dw, part, B, cin, cout, ld, (int)S, st);
+  } else if (vec_ok<T>(ld))
     hipLaunchKernelGGL((psa::psa_conv_dw_kernel<T, true>), dim3((unsigned)gw), dim3(256), 0, st, (const T*)x,
                        (const T*)dy, (T*)dw, part, B, cin, cout, ld, n_citiles, n_cotiles, (int)S, gw);
   else
@@ -423,9 +430,9 @@ int run_conv_bwd(const void* x, const void* w, const void* dy, const psa::DxPart
                        (const T*)dy, (T*)dw, part, B, cin, cout, ld, n_citiles, n_cotiles, (int)S, gw);
   rc = check_launch("psa_qkv_conv_bwd dw launch");
   if (rc == PSA_OK && S > 1) {
-    const long long n = (long long)cout * cin;
-    hipLaunchKernelGGL((psa::psa_conv_dw_reduce_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       (const float*)part, (T*)dw, n, (int)S);
+    const long long n4 = (long long)cout * cin / 4;  // cin is a multiple of 128
+    hipLaunchKernelGGL((psa::psa_conv_dw_reduce_kernel<T>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)part, (T*)dw, n4, (int)S);
     rc = check_launch("psa_qkv_conv_bwd dw reduce launch");
   }
   return rc;

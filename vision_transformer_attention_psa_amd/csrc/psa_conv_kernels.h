@@ -222,15 +222,18 @@ __global__ __launch_bounds__(256) void psa_conv_dw_kernel(const T* __restrict__ 
       }
 }
 
-// dw = sum over s of part[s], in s order.
+// dw = sum over s of part[s], in s order; n4 = cout * cin / 4 (cin is a
+// multiple of 128), four consecutive elements per thread.
 template <typename T>
 __global__ __launch_bounds__(256) void psa_conv_dw_reduce_kernel(const float* __restrict__ part, T* __restrict__ dw,
-                                                                 long long n, int n_splits) {
+                                                                 long long n4, int n_splits) {
   const long long i = (long long)block_id() * 256 + thread_id();
-  if (i >= n) return;
-  float v = part[i];
-  for (int s = 1; s < n_splits; ++s) v += part[(size_t)s * n + i];
-  dw[i] = from_f32<T>(v);
+  if (i >= n4) return;
+  const f32x4* p = (const f32x4*)part + i;
+  f32x4 v = p[0];
+  for (int s = 1; s < n_splits; ++s) v += p[(size_t)s * n4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dw[4 * i + q] = from_f32<T>(v[q]);
 }
 
 // ------------------------------------------------------------ row copies

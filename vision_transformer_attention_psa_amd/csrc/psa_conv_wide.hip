@@ -15,6 +15,10 @@
 // of a channel concatenation (see DxParts), as psa_conv_dx_kernel does.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
+#include <type_traits>
+
 #include "psa_conv_wide.h"
 #include "psa_conv_kernels.h"
 
@@ -180,6 +184,148 @@ void psa_conv_dx_pipe_kernel(const T* __restrict__ w, const T* __restrict__ dy, 
     }
 }
 
+// dw[co][ci] = sum_b sum_n dy[b][co][n] x[b][ci][n] over 128 co x 256 ci
+// workgroup tiles, for rows of ld tokens (a multiple of 8; tokens in [N, ld)
+// are the zeros of the caller's padded copies).  Workgroup: tile rr and
+// range s of the (b, 64-token stage) sequence, cut into n_splits contiguous
+// ranges as in psa_conv_dw_kernel (fp32 partials when n_splits > 1).
+// 8 waves, two per SIMD: wave w computes the 128 co x 64 ci block at ci
+// column 64 (w & 3) over the 32-token half (w >> 2) of every stage, so a
+// wave reads 12 fragments per 32 MFMAs while the workgroup's partial stays
+// the size of its tile; at the end each wave adds its partner's sums of
+// half of the rows (through LDS) and writes them.  The operand tiles come
+// into LDS by direct loads through a ring of 3 stage slots, two stages
+// ahead.  Each 1 KB load fills 8 rows of 128 bytes, and 16-byte chunk c of
+// row p holds the row's token chunk c ^ p: the 8 rows that a fragment read
+// takes at one token chunk sit on 8 different 16-byte bank groups.
+template <typename T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void psa_conv_dw_pipe_kernel(const T* __restrict__ x, const T* __restrict__ dy, T* __restrict__ dw,
+                             float* __restrict__ part, int cin, int cout, int ld, int n_citiles, int nchunk,
+                             int n_splits, int n_blocks) {
+  constexpr int BM = 128, BN = 256, BT = 64;  // co rows, ci rows, tokens per stage
+  constexpr int RB = BT * (int)sizeof(T);     // bytes per row of a stage
+  constexpr int RPL = 1024 / RB;              // rows per 1 KB load
+  constexpr int NA = BM / RPL, NB = BN / RPL, NW = 8;
+  constexpr int AI = NA / NW, BI = NB / NW, L = AI + BI;  // loads per wave per stage
+  constexpr int IB = 1024, SB = (NA + NB) * IB;            // bytes per load slot, per stage
+  constexpr int IA = BM / 16, JN = 4;                      // fragments per wave: co, ci
+  static_assert(RPL == 8 && NA % NW == 0 && NB % NW == 0, "stage layout");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * SB];
+  static_assert(NW * (IA / 2) * JN * 64 * 16 <= 3 * SB, "exchange area");
+
+  const int tid = thread_id(), lane = tid & 63, g = lane >> 4, t = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), h = wv >> 2, wq = wv & 3;
+  const int blk = xcd_remap(block_id(), n_blocks);
+  const int tiles = n_citiles * (cout / BM);
+  const int s = blk / tiles, rr = blk - s * tiles;
+  const int cot = rr / n_citiles, co0 = cot * BM, ci0 = (rr - cot * n_citiles) * BN;
+  const int cps = (ld + BT - 1) / BT;  // stages per batch
+  const int c0 = (int)((long long)nchunk * s / n_splits), c1 = (int)((long long)nchunk * (s + 1) / n_splits);
+
+  // This lane's part of each load: row p = lane / 8 of the load's 8, token
+  // chunk (lane % 8) ^ p; byte offsets from the tile's first row.
+  const int p = lane >> 3, tokl = 8 * ((lane & 7) ^ p);
+  unsigned a_row[AI], b_row[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) a_row[i] = (unsigned)((RPL * (wv * AI + i) + p) * ld) * (unsigned)sizeof(T);
+#pragma unroll
+  for (int i = 0; i < BI; ++i) b_row[i] = (unsigned)((RPL * (wv * BI + i) + p) * ld) * (unsigned)sizeof(T);
+  auto issue = [&](int ck, int slot) {
+    const int b = ck / cps, nn = (ck - b * cps) * BT;
+    const T* ya = dy + ((size_t)b * cout + co0) * ld;
+    const T* xb = x + ((size_t)b * cin + ci0) * ld;
+    const unsigned char* sb = smem + slot * SB;
+    // chunks past the row end (the batch's last stage) re-read its last
+    // chunk; their fragments are zeroed before use
+    const unsigned to = (unsigned)min(nn + tokl, ld - 8) * (unsigned)sizeof(T);
+#pragma unroll
+    for (int i = 0; i < AI; ++i) lds_dma16(ya, a_row[i] + to, sb + (wv * AI + i) * IB);
+#pragma unroll
+    for (int i = 0; i < BI; ++i) lds_dma16(xb, b_row[i] + to, sb + (NA + wv * BI + i) * IB);
+  };
+  // Fragment reads: lane (t, g) reads row 16 i + t (co) or 64 wq + 16 j + t
+  // (ci) at token chunk 4 h + g of the stage; rows 16 i .. 16 i + 15 are the
+  // loads 2 i and 2 i + 1.
+  const int jc = 4 * h + g, pr = t & 7;
+  const int rd = (t >> 3) * IB + pr * RB + 16 * (jc ^ pr);
+  const unsigned char* abase = smem + rd;
+  const unsigned char* bbase = smem + (NA + 8 * wq) * IB + rd;
+
+  f32x4 acc[IA][JN];
+#pragma unroll
+  for (int i = 0; i < IA; ++i)
+#pragma unroll
+    for (int j = 0; j < JN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = c1 - c0;
+  if (nk > 0) issue(c0, 0);
+  if (nk > 1) issue(c0 + 1, 1);
+  for (int k = 0; k < nk; ++k) {
+    // this wave's loads of stage k done (those of k + 1 may fly), then
+    // everyone's; every wave is past its reads of stage k - 1
+    if (k + 1 < nk)
+      barrier_vmcnt<L>();
+    else
+      barrier_vmcnt<0>();
+    if (k + 2 < nk) issue(c0 + k + 2, (k + 2) % 3);
+    const int so = (k % 3) * SB;
+    typedef typename Vec8<T>::type V8;
+    Frag<T> fa[IA], fb[JN];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) fb[j].v = *(const V8*)(bbase + so + 2 * j * IB);
+#pragma unroll
+    for (int i = 0; i < IA; ++i) fa[i].v = *(const V8*)(abase + so + 2 * i * IB);
+    const int ck = c0 + k, nn = (ck - (ck / cps) * cps) * BT;
+    if (nn + BT > ld && nn + 8 * jc >= ld) {  // past the row end: zero
+#pragma unroll
+      for (int j = 0; j < JN; ++j) fb[j].v = V8{};
+#pragma unroll
+      for (int i = 0; i < IA; ++i) fa[i].v = V8{};
+    }
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) mma(acc[i][j], fa[i], fb[j]);
+  }
+
+  // Halves: wave (h, wq) keeps rows i in [4 h, 4 h + 4) and hands the other
+  // four to its partner (1 - h, wq); the sum is lower half + upper half.
+  // (H is a constant in each branch: an index that varies at run time
+  // would put the accumulators in scratch memory.)
+  constexpr int IH = IA / 2;
+  f32x4* ex = (f32x4*)smem;
+  auto finish = [&](auto hc) {
+    constexpr int H = decltype(hc)::value;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < IH; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) ex[(((wq * 2 + H) * IH + i) * JN + j) * 64 + lane] = acc[(1 - H) * IH + i][j];
+    __syncthreads();
+    // acc[i][j]: row co0 + 16 i + 4 g + q, column ci0 + 64 wq + 16 j + t.
+#pragma unroll
+    for (int i = 0; i < IH; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        const f32x4 o = ex[(((wq * 2 + 1 - H) * IH + i) * JN + j) * 64 + lane];
+        const f32x4 v = H == 0 ? acc[i][j] + o : o + acc[IH + i][j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const size_t e = (size_t)(co0 + 16 * (H * IH + i) + 4 * g + q) * cin + ci0 + 64 * wq + 16 * j + t;
+          if (n_splits == 1)
+            dw[e] = from_f32<T>(v[q]);
+          else
+            part[(size_t)s * cout * cin + e] = v[q];
+        }
+      }
+  };
+  if (h == 0)
+    finish(std::integral_constant<int, 0>{});
+  else
+    finish(std::integral_constant<int, 1>{});
+}
+
 namespace {
 
 // The pipeline needs this many workgroups (one per CU) to pay off.
@@ -212,7 +358,36 @@ void launch(DxLarge kind, const void* w, const void* dy, const DxParts<T>& dx, i
   }
 }
 
+template <typename T>
+void dw_pipe(const void* x, const void* dy, void* dw, float* part, int B, int cin, int cout, int ld, int S,
+             hipStream_t st) {
+  const int n_citiles = cin / 256, tiles = n_citiles * (cout / 128), blocks = tiles * S;
+  const int nchunk = B * ((ld + 63) / 64);
+  hipLaunchKernelGGL((psa_conv_dw_pipe_kernel<T>), dim3(blocks), dim3(512), 0, st, (const T*)x, (const T*)dy, (T*)dw,
+                     part, cin, cout, ld, n_citiles, nchunk, S, blocks);
+}
+
 }  // namespace
+
+int conv_dw_pipe_splits(int B, int cin, int cout, int ld, int cus) {
+  if (ld % 8 != 0 || cin % 256 != 0 || cout % 128 != 0) return 0;
+  if ((long long)256 * ld * 2 >= INT32_MAX) return 0;  // 32-bit byte offsets within a tile's rows
+  const long long tiles = (long long)(cin / 256) * (cout / 128);
+  const long long nchunk = (long long)B * ((ld + 63) / 64);
+  // one workgroup per CU (its LDS ring takes 144 KB), each range >= 4 stages
+  long long S = std::min<long long>(cus / tiles, std::min<long long>(64, nchunk / 4));
+  if (S < 1 || tiles * S < (3LL * cus) / 4) return 0;  // too few workgroups to fill the CUs
+  return (int)S;
+}
+
+void conv_dw_pipe_launch(const bf16* x, const bf16* dy, bf16* dw, float* part, int B, int cin, int cout, int ld,
+                         int S, hipStream_t st) {
+  dw_pipe<bf16>(x, dy, dw, part, B, cin, cout, ld, S, st);
+}
+void conv_dw_pipe_launch(const f16* x, const f16* dy, f16* dw, float* part, int B, int cin, int cout, int ld,
+                         int S, hipStream_t st) {
+  dw_pipe<f16>(x, dy, dw, part, B, cin, cout, ld, S, st);
+}
 
 DxLarge conv_dx_large_kind(int B, int cin, int N, int ld) {
   if (ld % 8 != 0) return DxLarge::none;  // 16-byte rows of a 16-bit type only

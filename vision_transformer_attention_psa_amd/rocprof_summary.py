@@ -27,6 +27,7 @@ PSA_SLOTS = (("psa_fwd_kernel", "fwd"), ("psa_bwd_pre_kernel", "bwd_pre"),
              ("psa_bwd_fused_kernel", "bwd_main"), ("psa_conv_dx_kernel", "conv_dx"),
              ("psa_conv_dx_pipe_kernel", "conv_dx_pipe"), ("psa_pad_rows_kernel", "pad_rows"),
              ("psa_conv_dw_reduce_kernel", "conv_dw_reduce"), ("psa_conv_dw_kernel", "conv_dw"),
+             ("psa_conv_dw_pipe_kernel", "conv_dw_pipe"),
              ("psa_rows_copy_kernel", "rows_copy"))
 
 
