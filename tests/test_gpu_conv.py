@@ -35,6 +35,8 @@ SHAPES = [
     # rows padded to 1008 with a 48-token last stage
     (inputs.F16, 4, 512, 1024, 6408),
     (inputs.F16, 8, 512, 1024, 1001),
+    # 192 tiles fill the CUs on their own: one range, dw written directly
+    (inputs.BF16, 1, 4096, 1536, 200),
 ]
 
 
